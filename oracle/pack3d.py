@@ -1,0 +1,413 @@
+"""Plain fp64 NumPy oracle of PACK3D (forward and backward).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``; never by the HIP library.
+
+What is computed ("Geometry Matters in Packed 3D Attention", abstract):
+
+* A packed volume is a sequence of tokens, each carrying its true integer
+  grid coordinate (z, y, x).  The packing order is arbitrary; only the
+  coordinates define geometry.
+* The volume is cut into contiguous 3D blocks of shape (bz, by, bx).  Reading
+  (block-granular locality): a query attends exactly to every key whose block
+  lies within Chebyshev distance ``r`` (in block units) of the query's block,
+  truncated at the volume edge, and to one summary per remaining block of the
+  same volume.
+* Axial RoPE on the true grid coordinates rotates Q and K, head dim split into
+  three contiguous groups (z, y, x).  Within a group of width d_a the pairs are
+  (k, k + d_a/2), with frequency theta_k = base^(-2k/d_a), the same set on
+  every axis (the convention of the "SpatioTemporal RoPE" section of the
+  HorizonStream post, reduced to three axes).
+* The rotation is applied before a block is summarized: the block summary is
+  the mean of the block's *rotated* keys and the mean of its values, so a
+  query-summary logit is the mean of that query's logits to the block's keys.
+* Local logits and summary logits share one softmax (scale 1/sqrt(D) unless
+  given).
+
+Readings where the pages are silent (each listed in the design notes):
+block lattice anchored at each volume's componentwise minimum coordinate; only
+full grids with extents divisible by the block are accepted; no causal mask;
+V is not rotated; lse is the natural-log log-sum-exp of the scaled logits;
+gradients are taken with respect to the unrotated q, k, v.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+
+class CoordsError(ValueError):
+    """Invalid geometry: ``reason`` in {"grid", "divisible", "duplicate"}."""
+
+    def __init__(self, volume: int, reason: str, token: int = -1):
+        super().__init__(f"volume {volume}: {reason} (token {token})")
+        self.volume, self.reason, self.token = volume, reason, token
+
+
+# --------------------------------------------------------------------------
+# Index: block membership, canonical order, neighbour table
+# --------------------------------------------------------------------------
+
+def _volume_index(c: np.ndarray, block, r: int, volume: int) -> dict:
+    """Tables of one volume.  ``c`` int [N, 3] (z, y, x)."""
+    c = c.astype(np.int64)
+    n = c.shape[0]
+    b = np.asarray(block, dtype=np.int64)
+    origin = c.min(axis=0)
+    extent = c.max(axis=0) - origin + 1
+    if int(np.prod(extent)) != n:
+        raise CoordsError(volume, "grid")
+    if np.any(extent % b):
+        raise CoordsError(volume, "divisible")
+    rel = c - origin
+    # Duplicates: a token is offending when an earlier token has the same point.
+    lin = (rel[:, 0] * extent[1] + rel[:, 1]) * extent[2] + rel[:, 2]
+    first = np.full(n, n, dtype=np.int64)
+    np.minimum.at(first, lin, np.arange(n))
+    dup = np.nonzero(first[lin] != np.arange(n))[0]
+    if dup.size:
+        raise CoordsError(volume, "duplicate", int(dup.min()))
+    nb = extent // b
+    bvol = int(np.prod(b))
+    beta = rel // b
+    blk = (beta[:, 0] * nb[1] + beta[:, 1]) * nb[2] + beta[:, 2]
+    w = rel - beta * b
+    omega = (w[:, 0] * b[1] + w[:, 1]) * b[2] + w[:, 2]
+    canon = blk * bvol + omega
+    perm = np.empty(n, dtype=np.int64)
+    perm[canon] = np.arange(n)
+    nblk = int(np.prod(nb))
+    offsets = list(itertools.product(range(-r, r + 1), repeat=3))  # (dz, dy, dx) raster
+    nbr = np.full((nblk, len(offsets)), -1, dtype=np.int64)
+    for bid in range(nblk):
+        bz, rem = divmod(bid, int(nb[1] * nb[2]))
+        by, bx = divmod(rem, int(nb[2]))
+        for s, (dz, dy, dx) in enumerate(offsets):
+            z, y, x = bz + dz, by + dy, bx + dx
+            if 0 <= z < nb[0] and 0 <= y < nb[1] and 0 <= x < nb[2]:
+                nbr[bid, s] = (z * nb[1] + y) * nb[2] + x
+    return dict(origin=origin, extent=extent, nb=nb, nblk=nblk, bvol=bvol, block=b,
+                token_block=blk, canon=canon, perm=perm, nbr=nbr, radius=r)
+
+
+def build_index(coords, block_shape, local_radius: int) -> list:
+    """Per-volume tables for coords int [B, N, 3] (z, y, x).
+
+    Raises ``CoordsError`` for the first bad volume (holes / not a full grid,
+    extents not divisible by the block, duplicate points) and ``ValueError``
+    for a bad block shape or a negative radius.
+    """
+    coords = np.asarray(coords)
+    if coords.ndim == 2:
+        coords = coords[None]
+    if len(block_shape) != 3 or min(block_shape) <= 0:
+        raise ValueError("block_shape must hold three positive extents")
+    if local_radius < 0:
+        raise ValueError("local_radius must be >= 0")
+    return [_volume_index(coords[v], block_shape, int(local_radius), v) for v in range(coords.shape[0])]
+
+
+# --------------------------------------------------------------------------
+# Axial RoPE
+# --------------------------------------------------------------------------
+
+def rope_tables(d_axis: int, base: float) -> np.ndarray:
+    """theta_k = base^(-2k/d_a), k = 0 .. d_a/2 - 1 (same set on every axis)."""
+    if d_axis % 2:
+        raise ValueError("per-axis width must be even")
+    k = np.arange(d_axis // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * k / d_axis)
+
+
+def rope(x, coords, base: float = 10000.0, inverse: bool = False) -> np.ndarray:
+    """Rotate x [N, H, D] (or [N, D]) by the axial RoPE of coords [N, 3].
+
+    Head dim = three contiguous groups (z, y, x) of width d_a = D/3; inside a
+    group, element k pairs with element k + d_a/2 and turns by angle
+    coord_a * theta_k:  (x1, x2) -> (x1 cos - x2 sin, x1 sin + x2 cos).
+    ``inverse`` applies the transpose (rotation by minus the angle).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    squeeze = x.ndim == 2
+    if squeeze:
+        x = x[:, None, :]
+    d = x.shape[-1]
+    if d % 6:
+        raise ValueError("head_dim must split into three even axis groups")
+    da, half = d // 3, d // 6
+    theta = rope_tables(da, base)
+    c = np.asarray(coords, dtype=np.float64)
+    sign = -1.0 if inverse else 1.0
+    out = np.empty_like(x)
+    for a in range(3):
+        phi = c[:, a, None] * theta[None, :]           # [N, half]
+        cos = np.cos(phi)[:, None, :]
+        sin = sign * np.sin(phi)[:, None, :]
+        x1 = x[..., a * da: a * da + half]
+        x2 = x[..., a * da + half: (a + 1) * da]
+        out[..., a * da: a * da + half] = x1 * cos - x2 * sin
+        out[..., a * da + half: (a + 1) * da] = x1 * sin + x2 * cos
+    return out[:, 0, :] if squeeze else out
+
+
+def pool_blocks(x_canon: np.ndarray, bvol: int) -> np.ndarray:
+    """Mean over each block of a canonical-order array [N, ...] -> [nblk, ...]."""
+    n = x_canon.shape[0]
+    return x_canon.reshape(n // bvol, bvol, *x_canon.shape[1:]).mean(axis=1)
+
+
+def unpool_grad(dbar: np.ndarray, bvol: int) -> np.ndarray:
+    """Gradient of the block mean: every member of block b receives dbar_b / |b| (canonical order)."""
+    return np.repeat(dbar, bvol, axis=0) / bvol
+
+
+# --------------------------------------------------------------------------
+# Forward
+# --------------------------------------------------------------------------
+
+def _f64(t) -> np.ndarray:
+    """Exact conversion of a numpy array or a CPU torch tensor to fp64 numpy."""
+    if hasattr(t, "detach"):
+        t = t.detach().to("cpu")
+        import torch  # local: the oracle itself does not need torch
+        return t.to(torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None):
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords)
+    if coords.ndim == 2:
+        coords = coords[None]
+    index = build_index(coords, block_shape, r)
+    rc = coords if rope_coords is None else np.asarray(rope_coords)
+    vols = []
+    for vi, ix in enumerate(index):
+        perm = ix["perm"]
+        qt = rope(q[vi][perm], rc[vi][perm], base)
+        kt = rope(k[vi][perm], rc[vi][perm], base)
+        vc = v[vi][perm]
+        vols.append(dict(ix=ix, qt=qt, kt=kt, vc=vc,
+                         kbar=pool_blocks(kt, ix["bvol"]), vbar=pool_blocks(vc, ix["bvol"])))
+    return q, k, v, coords, vols
+
+
+def _local_blocks(ix, qb):
+    return [int(n) for n in ix["nbr"][qb] if n >= 0]
+
+
+def _summary_blocks(ix, qb, local):
+    mask = np.ones(ix["nblk"], dtype=bool)
+    mask[local] = False
+    return np.nonzero(mask)[0]
+
+
+def _key_rows(local, bvol):
+    return np.concatenate([np.arange(n * bvol, (n + 1) * bvol) for n in local])
+
+
+def forward(q, k, v, coords, block_shape, local_radius, *, rope_base=10000.0, scale=None,
+            with_summaries=True, query_blocks=None, rope_coords=None, return_logits=False):
+    """PACK3D forward.  q, k, v [B, N, H, D]; coords [B, N, 3] (z, y, x).
+
+    Returns (o [B, N, H, D], lse [B, H, N]) in fp64, packed order.  With
+    ``query_blocks`` (a list of block ids) only those query blocks are
+    computed in every volume; other rows are NaN.  ``return_logits`` (tiny
+    inputs only) adds dense [B, H, N, N] local and [B, H, N, nblk] summary
+    logit matrices, NaN where a pair is not in the set.
+    """
+    q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base, rope_coords)
+    bsz, n, h, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = np.full((bsz, n, h, d), np.nan)
+    lse = np.full((bsz, h, n), np.nan)
+    if return_logits:
+        lg_loc = np.full((bsz, h, n, n), np.nan)
+        lg_sum = np.full((bsz, h, n, vols[0]["ix"]["nblk"]), np.nan)
+    for vi, vol in enumerate(vols):
+        ix = vol["ix"]
+        bvol, perm = ix["bvol"], ix["perm"]
+        qbs = range(ix["nblk"]) if query_blocks is None else query_blocks
+        for qb in qbs:
+            rows = np.arange(qb * bvol, (qb + 1) * bvol)
+            local = _local_blocks(ix, qb)
+            krows = _key_rows(local, bvol)
+            qt = vol["qt"][rows].transpose(1, 0, 2)                          # [H, bq, D]
+            s = scale * (qt @ vol["kt"][krows].transpose(1, 2, 0))           # [H, bq, nk]
+            parts = [s]
+            sb = _summary_blocks(ix, qb, local) if with_summaries else np.zeros(0, dtype=np.int64)
+            use_sum = sb.size > 0
+            if use_sum:
+                t = scale * (qt @ vol["kbar"][sb].transpose(1, 2, 0))        # [H, bq, ns]
+                parts.append(t)
+            m = np.max(np.concatenate([p.max(axis=-1, keepdims=True) for p in parts], -1), -1, keepdims=True)
+            es = np.exp(s - m)
+            acc = es @ vol["vc"][krows].transpose(1, 0, 2)                   # [H, bq, D]
+            den = es.sum(-1, keepdims=True)
+            if use_sum:
+                et = np.exp(t - m)
+                acc = acc + et @ vol["vbar"][sb].transpose(1, 0, 2)
+                den = den + et.sum(-1, keepdims=True)
+            src = perm[rows]                                                 # packed positions
+            o[vi, src] = (acc / den).transpose(1, 0, 2)
+            lse[vi][:, src] = (m + np.log(den))[..., 0]
+            if return_logits:
+                kp = perm[krows]
+                lg_loc[vi][:, src[:, None], kp[None, :]] = s
+                if use_sum:
+                    lg_sum[vi][:, src[:, None], sb[None, :]] = t
+    if return_logits:
+        return o, lse, lg_loc, lg_sum
+    return o, lse
+
+
+def forward_naive(q, k, v, coords, block_shape, local_radius, *, rope_base=10000.0, scale=None,
+                  with_summaries=True):
+    """The definition token by token, with no index tables (tiny inputs only).
+
+    Membership is decided by brute force: key j is local to query i when the
+    Chebyshev distance between their block coordinates is <= r; every other
+    block of the volume contributes one summary, the mean of its rotated keys
+    and of its values.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords).astype(np.int64)
+    bsz, n, h, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    b = np.asarray(block_shape, dtype=np.int64)
+    o = np.zeros((bsz, n, h, d))
+    lse = np.zeros((bsz, h, n))
+    for vi in range(bsz):
+        c = coords[vi]
+        bc = (c - c.min(axis=0)) // b                      # block coordinate of every token
+        qt = rope(q[vi], c, rope_base)
+        kt = rope(k[vi], c, rope_base)
+        blocks = sorted({tuple(x) for x in bc.tolist()})
+        members = {blk: np.nonzero((bc == np.asarray(blk)).all(axis=1))[0] for blk in blocks}
+        kbar = {blk: kt[idx].mean(axis=0) for blk, idx in members.items()}
+        vbar = {blk: v[vi][idx].mean(axis=0) for blk, idx in members.items()}
+        for i in range(n):
+            cheb_tok = np.abs(bc - bc[i]).max(axis=1)
+            loc = np.nonzero(cheb_tok <= local_radius)[0]
+            far = [blk for blk in blocks if max(abs(x - y) for x, y in zip(blk, bc[i])) > local_radius]
+            for hh in range(h):
+                logits = [scale * (kt[loc, hh] @ qt[i, hh])]
+                vals = [v[vi][loc, hh]]
+                if with_summaries and far:
+                    logits.append(np.array([scale * (kbar[blk][hh] @ qt[i, hh]) for blk in far]))
+                    vals.append(np.stack([vbar[blk][hh] for blk in far]))
+                lg = np.concatenate(logits)
+                vv = np.concatenate(vals)
+                m = lg.max()
+                e = np.exp(lg - m)
+                o[vi, i, hh] = e @ vv / e.sum()
+                lse[vi, hh, i] = m + np.log(e.sum())
+    return o, lse
+
+
+def dense_attention(q, k, v, coords, *, rope_base=10000.0, scale=None):
+    """Textbook softmax attention over every token of the volume, with 3D RoPE."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords)
+    bsz, n, h, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = np.empty_like(q)
+    lse = np.empty((bsz, h, n))
+    for vi in range(bsz):
+        qt = rope(q[vi], coords[vi], rope_base).transpose(1, 0, 2)
+        kt = rope(k[vi], coords[vi], rope_base).transpose(1, 0, 2)
+        s = scale * qt @ kt.transpose(0, 2, 1)
+        m = s.max(-1, keepdims=True)
+        e = np.exp(s - m)
+        o[vi] = (e @ v[vi].transpose(1, 0, 2) / e.sum(-1, keepdims=True)).transpose(1, 0, 2)
+        lse[vi] = (m + np.log(e.sum(-1, keepdims=True)))[..., 0]
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+
+def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.0, scale=None,
+             with_summaries=True, volumes=None, heads=None):
+    """Gradients (dq, dk, dv) [B, N, H, D] fp64 of sum(o * do) w.r.t. unrotated q, k, v.
+
+    With o_i = (sum_j P_ij V_j + sum_b P_ib Vbar_b), P = exp(logit - lse_i):
+      delta_i = <dO_i, o_i>
+      dS_ij = P_ij (<dO_i, V_j> - delta_i),  dT_ib = P_ib (<dO_i, Vbar_b> - delta_i)
+      dQ~_i = scale (sum_j dS_ij K~_j + sum_b dT_ib Kbar_b)
+      dK~_j = scale sum_i dS_ij Q~_i + dKbar_b(j) / |b|,  dKbar_b = scale sum_i dT_ib Q~_i
+      dV_j  = sum_i P_ij dO_i + dVbar_b(j) / |b|,         dVbar_b = sum_i P_ib dO_i
+      dq = R(c)^T dQ~, dk = R(c)^T dK~  (the mean pooling broadcasts 1/|b| to its members).
+    ``volumes`` / ``heads`` restrict the work (other entries are NaN).
+    """
+    q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base)
+    do = _f64(do)
+    bsz, n, h, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = np.full_like(q, np.nan)
+    dk = np.full_like(q, np.nan)
+    dv = np.full_like(q, np.nan)
+    vsel = range(bsz) if volumes is None else volumes
+    hsel = np.arange(h) if heads is None else np.asarray(heads)
+    for vi in vsel:
+        vol = vols[vi]
+        ix = vol["ix"]
+        bvol, perm, nblk = ix["bvol"], ix["perm"], ix["nblk"]
+        qt_all, kt_all, vc_all = vol["qt"][:, hsel], vol["kt"][:, hsel], vol["vc"][:, hsel]
+        kbar, vbar = vol["kbar"][:, hsel], vol["vbar"][:, hsel]
+        doc = do[vi][perm][:, hsel]
+        dqt = np.zeros_like(qt_all)
+        dkt = np.zeros_like(kt_all)
+        dvc = np.zeros_like(vc_all)
+        dkbar = np.zeros_like(kbar)
+        dvbar = np.zeros_like(vbar)
+        for qb in range(nblk):
+            rows = np.arange(qb * bvol, (qb + 1) * bvol)
+            local = _local_blocks(ix, qb)
+            krows = _key_rows(local, bvol)
+            qt = qt_all[rows].transpose(1, 0, 2)                 # [H, bq, D]
+            kk = kt_all[krows].transpose(1, 0, 2)                # [H, nk, D]
+            vv = vc_all[krows].transpose(1, 0, 2)
+            dob = doc[rows].transpose(1, 0, 2)                   # [H, bq, D]
+            s = scale * qt @ kk.transpose(0, 2, 1)
+            logits = [s]
+            sb = _summary_blocks(ix, qb, local) if with_summaries else np.zeros(0, dtype=np.int64)
+            use_sum = sb.size > 0
+            if use_sum:
+                kb = kbar[sb].transpose(1, 0, 2)
+                vb = vbar[sb].transpose(1, 0, 2)
+                t = scale * qt @ kb.transpose(0, 2, 1)
+                logits.append(t)
+            m = np.max(np.concatenate([x.max(-1, keepdims=True) for x in logits], -1), -1, keepdims=True)
+            den = sum(np.exp(x - m).sum(-1, keepdims=True) for x in logits)
+            lse = m + np.log(den)
+            p = np.exp(s - lse)
+            ob = p @ vv
+            if use_sum:
+                pt = np.exp(t - lse)
+                ob = ob + pt @ vb
+            delta = (dob * ob).sum(-1, keepdims=True)            # [H, bq, 1]
+            ds = p * (dob @ vv.transpose(0, 2, 1) - delta)
+            dqb = ds @ kk
+            # krows lists each neighbour block once, so fancy-index accumulation is exact
+            dkt[krows] += (scale * ds.transpose(0, 2, 1) @ qt).transpose(1, 0, 2)
+            dvc[krows] += (p.transpose(0, 2, 1) @ dob).transpose(1, 0, 2)
+            if use_sum:
+                dt = pt * (dob @ vb.transpose(0, 2, 1) - delta)
+                dqb = dqb + dt @ kb
+                dkbar[sb] += (scale * dt.transpose(0, 2, 1) @ qt).transpose(1, 0, 2)
+                dvbar[sb] += (pt.transpose(0, 2, 1) @ dob).transpose(1, 0, 2)
+            dqt[rows] = scale * dqb.transpose(1, 0, 2)
+        dkt += unpool_grad(dkbar, bvol)
+        dvc += unpool_grad(dvbar, bvol)
+        c = coords[vi][perm]
+        dq_c = rope(dqt, c, rope_base, inverse=True)
+        dk_c = rope(dkt, c, rope_base, inverse=True)
+        for src, dst in ((dq_c, dq), (dk_c, dk), (dvc, dv)):
+            tmp = np.empty((n, len(hsel), d))
+            tmp[perm] = src
+            dst[vi][:, hsel] = tmp
+    return dq, dk, dv
