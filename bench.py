@@ -1,0 +1,213 @@
+#!/usr/bin/env python
+"""PACK3D benchmark on one MI355X: tokens/s and ms per step at 65,536 tokens per volume.
+
+Workload: 2 volumes of 32x32x64 = 65,536 tokens (131,072 per call), random
+packing, 8 heads, head dim 96, 4x4x4 blocks (1,024 per volume), local radius 1
+(3x3x3 blocks), bf16 with fp32 accumulation, synthetic N(0,1) inputs.
+
+A step is one pass of the hot path over that batch with the index already built
+(it depends on the geometry only and is built once, timed separately): the forward
+(RoPE/gather/pooling, fused attention) and, when the library provides it, the
+backward.  Inputs are resident in HBM before the timed region starts.
+
+Printed: one JSON line with the contract fields, the roofline of the dominant
+kernel (fused attention forward) from HIP events recorded by the library around
+each launch on its stream, the windowed-only (local keys only) latency of the same
+kernel, and the fp64 CPU oracle timed on a bounded sample (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "PACK3D fwd(+bwd) tokens/s and ms at 65k tokens; MFMA util % of peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pair_counts(tables: dict) -> tuple[int, int]:
+    """(local pairs, summary pairs) per (volume, head), from the neighbour table of volume 0."""
+    nbr = tables["nbr"][0].cpu()
+    bvol, nblk = tables["block_tokens"], tables["nblk"]
+    nloc = (nbr >= 0).sum(1).long()
+    local = int((nloc * bvol * bvol).sum())
+    summ = int(((nblk - nloc) * bvol).sum())
+    return local, summ
+
+
+def time_region(fn, steps: int):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1000.0 / steps
+
+
+def cpu_baseline(w, x, sample_blocks: int) -> dict:
+    """The fp64 oracle on the host cores: all heads of the first `sample_blocks` query blocks of each volume."""
+    import oracle  # test infrastructure, used only for this reported baseline
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS uses every core
+        cores = os.cpu_count() or 1
+    blocks = list(range(sample_blocks))
+    t0 = time.perf_counter()
+    oracle.forward(x["q"], x["k"], x["v"], x["coords"], w.block, w.radius, query_blocks=blocks)
+    dt = time.perf_counter() - t0
+    tokens = w.batch * sample_blocks * int(w.block[0] * w.block[1] * w.block[2])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"forward only: {sample_blocks} of {w.tokens // (w.block[0] * w.block[1] * w.block[2])} "
+                      f"query blocks per volume, all {w.heads} heads, both volumes ({tokens} query tokens), "
+                      f"fp64 NumPy, {dt:.1f} s including the whole-volume RoPE and pooling"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="65k")
+    ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); the operator "
+              f"is benchmarked per GPU and this build has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+    import synthetic_inputs as si
+    import sparse_local_global_amd.pack3d as p3
+
+    w = si.WORKLOADS[args.workload]
+    dtype = torch.bfloat16
+    log(f"bench: generating {w.description}")
+    x = si.make_inputs(w, dtype, with_grad=True)
+    xd = {k: v.to("cuda:0") for k, v in x.items()}
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    ix = p3.build_index(xd["coords"], w.block, w.radius, order_hint=w.packing)
+    index_ms = (time.perf_counter() - t0) * 1000.0
+    attn = p3.make_attn(dtype, w.heads, w.head_dim, w.rope_base)
+    ws = torch.empty(p3.workspace_bytes(ix, attn, True), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(xd["q"])
+    lse = torch.empty((w.batch, w.heads, w.tokens), dtype=torch.float32, device="cuda:0")
+
+    with_bwd = not args.forward_only
+    if with_bwd:
+        try:
+            p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws)
+        except p3.Pack3DError as e:
+            if e.status != p3.E_UNSUPPORTED:
+                raise
+            log(f"bench: backward not available ({e}); timing the forward only")
+            with_bwd = False
+
+    def fwd(with_summaries=True):
+        p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], with_summaries=with_summaries,
+                   workspace=ws, out=out, lse=lse)
+
+    def step():
+        fwd()
+        if with_bwd:
+            p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    log(f"bench: warmup done ({args.warmup} steps), timing {args.steps} steps")
+    ms_step = time_region(step, args.steps)
+
+    # same steps again with per-kernel HIP events (library-side, on the launch stream)
+    p3.profile_reset()
+    p3.profile_enable(True)
+    ms_step_profiled = time_region(step, args.steps)
+    prof = p3.profile_read()
+    p3.profile_enable(False)
+
+    # windowed-only baseline: the same kernel with the summary stream off
+    for _ in range(args.warmup):
+        fwd(False)
+    ms_fwd = time_region(fwd, args.steps)
+    ms_win = time_region(lambda: fwd(False), args.steps)
+    p3.profile_reset()
+    p3.profile_enable(True)
+    time_region(lambda: fwd(False), args.steps)
+    prof_win = p3.profile_read()
+    p3.profile_enable(False)
+    log(f"bench: step {ms_step:.3f} ms, forward {ms_fwd:.3f} ms, windowed-only forward {ms_win:.3f} ms")
+
+    local, summ = pair_counts(ix.tables())
+    bh = w.batch * w.heads
+    d = w.head_dim
+    fwd_flop = 4.0 * d * (local + summ) * bh
+    win_flop = 4.0 * d * local * bh
+    kern = {k: {"launches": n, "avg_ms": t / max(n, 1)} for k, (n, t) in prof.items()}
+    attn_ms = kern["attn_fwd"]["avg_ms"]
+    win_attn_ms = prof_win["attn_fwd_windowed"][1] / max(prof_win["attn_fwd_windowed"][0], 1)
+    achieved = fwd_flop / (attn_ms * 1e-3) / 1e12
+    # rope/pool: reads q, k, v; writes rotated q, k and transposed v (block means are negligible)
+    elem = 2
+    rope_bytes = 6.0 * w.batch * w.tokens * w.heads * d * elem
+    rope_ms = kern["rope_pool"]["avg_ms"]
+
+    tokens = w.batch * w.tokens
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "65k", "pass": "forward+backward" if with_bwd else "forward",
+                   "batch": w.batch, "grid_zyx": list(w.grid), "tokens_per_volume": w.tokens,
+                   "tokens_per_step": tokens, "heads": w.heads, "head_dim": d, "block_zyx": list(w.block),
+                   "local_radius": w.radius, "packing": w.packing, "accumulation": "fp32"},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flop_per_launch": fwd_flop, "avg_launch_ms": attn_ms},
+        "kernels": kern,
+        "forward_ms": ms_fwd,
+        "windowed_forward_ms": ms_win,
+        "forward_vs_windowed": ms_fwd / ms_win,
+        "attn_vs_windowed_attn": attn_ms / win_attn_ms,
+        "windowed_attn": {"avg_ms": win_attn_ms, "tflops": win_flop / (win_attn_ms * 1e-3) / 1e12},
+        "rope_pool": {"avg_ms": rope_ms, "algorithmic_bytes": rope_bytes,
+                      "gbs": rope_bytes / (rope_ms * 1e-3) / 1e9,
+                      "frac_hbm": rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "index_build_ms": index_ms,
+        "ms_per_step_with_kernel_events": ms_step_profiled,
+        "pairs_per_volume_head": {"local": local, "summary": summ},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the fp64 oracle on {args.cpu_sample_blocks} query blocks per volume")
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_blocks)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,202 @@
+/*
+ * pack3d.h -- C ABI of the PACK3D local-global attention operator for MI355X (gfx950).
+ *
+ * The operator ("Geometry Matters in Packed 3D Attention", arXiv:2610.38694, abstract):
+ * every token of a packed 3D volume attends exactly to the keys of its 3D
+ * neighbourhood of blocks, and to one summary per distant contiguous 3D block,
+ * under one shared softmax.  Every query-key and query-summary logit is indexed by
+ * axial RoPE on the tokens' true (z, y, x) grid coordinates, never their packed
+ * position, and the rotation is applied before a block is summarized (a summary is
+ * the mean of the block's rotated keys and the mean of its values).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer named *_dev is device memory owned by the caller; the library
+ *     never allocates, frees or retains device memory.  It allocates only the small
+ *     host-side index handle (malloc/free).
+ *   - q, k, v, out, dout, dq, dk, dv are contiguous [B, N, H, D] arrays, D innermost,
+ *     in packed (caller) order, all of the dtype named in pack3d_attn.  lse is fp32
+ *     [B, H, N] in packed order.  coords is int32 [B, N, 3] holding (z, y, x).
+ *   - stream is a hipStream_t (NULL = the null stream).  Forward and backward are
+ *     asynchronous on it and never synchronize.  pack3d_build_index synchronizes the
+ *     stream once (to read back the geometry check).
+ *   - On any error nothing is launched (argument errors) and a message is kept in a
+ *     thread-local buffer returned by pack3d_last_error().  Launch failures return
+ *     PACK3D_E_HIP.
+ *   - Functions never throw and are safe to call from several host threads on
+ *     different handles; calls sharing a workspace must be serialized by the caller.
+ */
+#ifndef PACK3D_H
+#define PACK3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pack3d_status {
+  PACK3D_OK = 0,
+  PACK3D_E_INVALID = 1,     /* null pointer, non-positive size, bad radius or block shape */
+  PACK3D_E_COORDS = 2,      /* geometry rejected: not a full grid, extents not divisible
+                               by the block, or a duplicate point */
+  PACK3D_E_UNSUPPORTED = 3, /* valid request outside what the kernels implement */
+  PACK3D_E_WORKSPACE = 4,   /* caller buffer smaller than the size query returned */
+  PACK3D_E_HIP = 5          /* HIP runtime or launch error */
+} pack3d_status;
+
+typedef enum pack3d_dtype { PACK3D_F32 = 0, PACK3D_BF16 = 1 } pack3d_dtype;
+
+/* A hint only: results never depend on it (the coordinates alone define geometry). */
+typedef enum pack3d_order {
+  PACK3D_ORDER_ANY = 0,
+  PACK3D_ORDER_RASTER = 1,
+  PACK3D_ORDER_MORTON = 2,
+  PACK3D_ORDER_BLOCK_CONTIGUOUS = 3,
+  PACK3D_ORDER_RANDOM = 4
+} pack3d_order;
+
+/* Batch layout: `batch` volumes of `tokens_per_volume` tokens each. */
+typedef struct pack3d_packing {
+  int32_t batch;
+  int32_t tokens_per_volume;
+  int32_t order_hint; /* pack3d_order */
+} pack3d_packing;
+
+/* Attention parameters.
+ *   head_dim: D, split into three axis groups (z, y, x) of D/3 each; D % 6 == 0 and
+ *             D <= 128 (inside each group element k pairs with element k + D/6).
+ *   rope_base: base of the RoPE frequencies theta_k = base^(-2k/(D/3)) (e.g. 10000).
+ *   softmax_scale: <= 0 selects 1/sqrt(D).
+ *   with_summaries: 1 = PACK3D (local keys + distant block summaries),
+ *                   0 = windowed-only (local keys only; the latency baseline). */
+typedef struct pack3d_attn {
+  int32_t dtype; /* pack3d_dtype */
+  int32_t heads;
+  int32_t head_dim;
+  float rope_base;
+  float softmax_scale;
+  int32_t with_summaries;
+} pack3d_attn;
+
+/* Opaque host handle describing one geometry (built once, reused by every call). */
+typedef struct pack3d_index pack3d_index;
+
+/* Device views of the index tables (read-only; they live in the caller's tables_dev).
+ *   token_block [B, N]      block id of each packed token; blocks are numbered in raster
+ *                           order over the block grid (z slowest) of its volume
+ *   canon       [B, N]      canonical slot of each packed token: block id * |b| + raster
+ *                           offset inside the block
+ *   perm        [B, N]      packed index stored at each canonical slot (inverse of canon)
+ *   nbr         [B, nblk, slots]  block ids of the (2r+1)^3 neighbourhood of each block,
+ *                           slots in raster order over (dz, dy, dx) in [-r, r]^3, -1 outside
+ *                           the volume
+ *   geom        [B, 8]      origin (z, y, x) = componentwise minimum coordinate, extent
+ *                           (z, y, x), status, offending token (device copy)          */
+typedef struct pack3d_tables {
+  const int32_t* token_block;
+  const int32_t* canon;
+  const int32_t* perm;
+  const int32_t* nbr;
+  const int32_t* geom;
+  int32_t batch, tokens, nblk, block_tokens, slots, radius;
+  int32_t block_shape[3];
+  int32_t extent_max[3];
+} pack3d_tables;
+
+/* Device bytes needed for the index tables of this batch layout, block shape and
+ * radius; 0 if the arguments are invalid.  The count does not depend on the
+ * coordinates: a valid geometry has exactly N / |b| blocks per volume. */
+size_t pack3d_index_bytes(const pack3d_packing* packing, const int32_t block_shape[3],
+                          int32_t local_radius);
+
+/* Build the index of a batch of packed volumes.
+ *   coords_dev [B, N, 3] int32 (z, y, x) grid coordinates in packed order.
+ *   block_shape (bz, by, bx) >= 1 with bz*by*bx a multiple of 8; local_radius r in
+ *   block units (0 <= r <= 7): a query's local set is every key whose block is within
+ *   Chebyshev distance r of the query's block (truncated at the volume edge); every
+ *   other block of the same volume contributes one summary.
+ *   tables_dev / tables_bytes: caller device buffer of at least pack3d_index_bytes();
+ *   it must outlive the handle.
+ * Each volume's block lattice is anchored at its componentwise minimum coordinate.
+ * Rejected with PACK3D_E_COORDS (message names the volume and, for a duplicate, the
+ * lowest packed index whose point already occurs earlier): extents whose product is
+ * not N (holes), extents not divisible by the block, duplicate points.
+ * On success *out receives a handle to release with pack3d_index_free. */
+pack3d_status pack3d_build_index(const int32_t* coords_dev, const pack3d_packing* packing,
+                                 const int32_t block_shape[3], int32_t local_radius,
+                                 void* tables_dev, size_t tables_bytes, void* stream,
+                                 pack3d_index** out);
+
+/* Fill *out with device views of the tables and their sizes. */
+pack3d_status pack3d_index_tables(const pack3d_index* index, pack3d_tables* out);
+
+/* Host copy of one volume's origin and extent: out6 = (oz, oy, ox, ez, ey, ex). */
+pack3d_status pack3d_index_geometry(const pack3d_index* index, int32_t volume, int32_t out6[6]);
+
+void pack3d_index_free(pack3d_index* index);
+
+/* Device workspace bytes for pack3d_forward (for_backward = 0) or pack3d_backward
+ * (for_backward = 1); 0 if the request is invalid or unsupported. */
+size_t pack3d_workspace_bytes(const pack3d_index* index, const pack3d_attn* attn, int for_backward);
+
+/* Forward.  Writes out [B, N, H, D] (attn->dtype) and lse [B, H, N] fp32: lse is the
+ * natural-log log-sum-exp of the scaled local and summary logits of each query.
+ * coords_dev must hold the coordinates the index was built from: the RoPE angles
+ * are taken from them (relative to each volume's origin, which leaves every logit
+ * unchanged).  Mismatched coordinates give unspecified values but no out-of-bounds
+ * access.  Precision: fp32 inputs are computed in fp32 throughout; bf16 inputs use
+ * bf16 matrix-core products with fp32 accumulation and fp32 softmax. */
+pack3d_status pack3d_forward(const pack3d_index* index, const pack3d_attn* attn,
+                             const void* q_dev, const void* k_dev, const void* v_dev,
+                             const int32_t* coords_dev, void* out_dev, float* lse_dev,
+                             void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* Backward of sum(out * dout): gradients dq, dk, dv [B, N, H, D] (attn->dtype) with
+ * respect to the unrotated q, k, v, through the RoPE and the block mean pooling.
+ * out_dev and lse_dev are the forward's outputs for the same inputs. */
+pack3d_status pack3d_backward(const pack3d_index* index, const pack3d_attn* attn,
+                              const void* q_dev, const void* k_dev, const void* v_dev,
+                              const int32_t* coords_dev, const void* out_dev,
+                              const float* lse_dev, const void* dout_dev, void* dq_dev,
+                              void* dk_dev, void* dv_dev, void* workspace_dev,
+                              size_t workspace_bytes, void* stream);
+
+/* Where the forward leaves its intermediates inside the workspace (byte offsets),
+ * for inspection by tests.  All arrays are in canonical order, elements of attn->dtype
+ * except rope_table (float2 cos, sin).
+ *   qrot, krot [B, H, N, Dp]            rotated Q and K, rows padded with zeros to Dp
+ *   vt         [B, H, nblk, Dp, |b|]    V transposed inside each block
+ *   kbar       [B, H, nblk_pad, Dp]     block means of the rotated K (zero padding rows)
+ *   vbart      [B, H, Dp, nblk_pad]     block means of V, transposed (zero padding)
+ * Rotation angles use coordinates relative to each volume's origin. */
+typedef struct pack3d_views {
+  size_t rope_table, qrot, krot, vt, kbar, vbart;
+  int32_t head_dim_padded, nblk_padded, extent_table;
+} pack3d_views;
+pack3d_status pack3d_workspace_views(const pack3d_index* index, const pack3d_attn* attn,
+                                     pack3d_views* out);
+
+/* Kernel timing, for measurement.  While enabled, every kernel launch made by
+ * pack3d_forward / pack3d_backward is bracketed by two HIP events recorded on the
+ * caller's stream (the stream the kernel runs on).  pack3d_profile_read waits for
+ * the recorded events, folds them into per-kernel totals and returns, for up to
+ * max_kernels kernels, the kernel name (NUL-separated in names, at most 47 bytes
+ * each), the number of launches and the summed milliseconds since the last reset;
+ * the return value is the number of kernels written, or -1 on a HIP error.
+ * Process-wide; enable before the calls to time, from one host thread. */
+pack3d_status pack3d_profile_enable(int32_t enable);
+int32_t pack3d_profile_read(char* names, size_t names_bytes, int32_t* launches, double* total_ms,
+                            int32_t max_kernels);
+void pack3d_profile_reset(void);
+
+/* Thread-local message describing the last error (empty string if none). */
+const char* pack3d_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int32_t pack3d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PACK3D_H */

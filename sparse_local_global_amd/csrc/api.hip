@@ -1,0 +1,108 @@
+// C ABI entry points of libpack3d: argument checks, workspace layout, dispatch.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "layout.h"
+
+namespace pack3d {
+
+static thread_local char g_msg[512] = "";
+
+pack3d_status set_error(pack3d_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pack3d_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(PACK3D_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PACK3D_OK;
+}
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+pack3d_status check_attn(const pack3d_index* ix, const pack3d_attn* at, const char* who) {
+  if (!ix || !at) return set_error(PACK3D_E_INVALID, "%s: null index or attention parameters", who);
+  if (at->dtype != PACK3D_F32 && at->dtype != PACK3D_BF16)
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: dtype %d is not supported", who, at->dtype);
+  if (at->heads < 1) return set_error(PACK3D_E_INVALID, "%s: heads must be >= 1", who);
+  if (at->head_dim < 6 || at->head_dim % 6 || at->head_dim > 128)
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: head_dim %d must be a multiple of 6 in [6, 128]", who, at->head_dim);
+  if (!(at->rope_base > 0.0f) || !std::isfinite(at->rope_base))
+    return set_error(PACK3D_E_INVALID, "%s: rope_base must be positive and finite", who);
+  if (!std::isfinite(at->softmax_scale))
+    return set_error(PACK3D_E_INVALID, "%s: softmax_scale must be finite", who);
+  if (ix->slots > kMaxSlots)
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: local radius %d > 3 is not supported by the attention kernels",
+                     who, ix->radius);
+  if (ix->nblk > kMaxBlocks)
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: %d blocks per volume > %d", who, ix->nblk, kMaxBlocks);
+  if (ix->bvol > kMaxBlockTokens)
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: %d tokens per block > %d", who, ix->bvol, kMaxBlockTokens);
+  if ((int64_t)ix->batch * at->heads * ix->tokens * padded_head_dim(at->head_dim) > ((int64_t)1 << 40))
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: problem too large", who);
+  return PACK3D_OK;
+}
+
+}  // namespace
+}  // namespace pack3d
+
+using namespace pack3d;
+
+extern "C" const char* pack3d_last_error(void) { return g_msg; }
+
+extern "C" int32_t pack3d_version(void) { return 100; }
+
+extern "C" size_t pack3d_workspace_bytes(const pack3d_index* ix, const pack3d_attn* at, int for_backward) {
+  if (check_attn(ix, at, "workspace_bytes") != PACK3D_OK) return 0;
+  Workspace w = workspace_layout(make_dims(ix, at));
+  return for_backward ? w.bwd_total : w.fwd_total;
+}
+
+extern "C" pack3d_status pack3d_workspace_views(const pack3d_index* ix, const pack3d_attn* at, pack3d_views* out) {
+  pack3d_status st = check_attn(ix, at, "workspace_views");
+  if (st != PACK3D_OK) return st;
+  if (!out) return set_error(PACK3D_E_INVALID, "workspace_views: null output");
+  Dims d = make_dims(ix, at);
+  Workspace w = workspace_layout(d);
+  out->rope_table = w.rope; out->qrot = w.qrot; out->krot = w.krot; out->vt = w.vt;
+  out->kbar = w.kbar; out->vbart = w.vbart;
+  out->head_dim_padded = d.Dp; out->nblk_padded = d.nblkp; out->extent_table = d.emax;
+  return PACK3D_OK;
+}
+
+extern "C" pack3d_status pack3d_forward(const pack3d_index* ix, const pack3d_attn* at, const void* q,
+                                        const void* k, const void* v, const int32_t* coords, void* out,
+                                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  pack3d_status st = check_attn(ix, at, "forward");
+  if (st != PACK3D_OK) return st;
+  if (!q || !k || !v || !coords || !out || !lse || !ws)
+    return set_error(PACK3D_E_INVALID, "forward: null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws))
+    return set_error(PACK3D_E_INVALID, "forward: q, k, v, out and workspace must be 16-byte aligned");
+  Dims d = make_dims(ix, at);
+  Workspace w = workspace_layout(d);
+  if (ws_bytes < w.fwd_total)
+    return set_error(PACK3D_E_WORKSPACE, "forward: workspace %zu bytes < %zu needed", ws_bytes, w.fwd_total);
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, s);
+  if (st != PACK3D_OK) return st;
+  return launch_attn_fwd(d, ix, at, (const char*)ws, w, out, lse, s);
+}
+
+extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_attn* at, const void* q,
+                                         const void* k, const void* v, const int32_t* coords,
+                                         const void* out, const float* lse, const void* dout, void* dq,
+                                         void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  pack3d_status st = check_attn(ix, at, "backward");
+  if (st != PACK3D_OK) return st;
+  (void)q; (void)k; (void)v; (void)coords; (void)out; (void)lse; (void)dout; (void)dq; (void)dk; (void)dv;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return set_error(PACK3D_E_UNSUPPORTED, "backward: not built yet");
+}

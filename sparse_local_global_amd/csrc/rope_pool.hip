@@ -1,0 +1,243 @@
+// K1 + K2: axial RoPE, gather into canonical order, and block mean pooling.
+//
+// "Geometry Matters in Packed 3D Attention" (abstract): every query-key and
+// query-summary interaction is indexed by axial RoPE on the true token-grid
+// coordinates, and the rotation is applied before a block is summarized.  So for
+// each token the head dim is cut into three contiguous groups (z, y, x) of width
+// d_a = D/3, element k of a group pairs with element k + d_a/2 and both turn by
+// angle coord_a * theta_k with theta_k = base^(-2k/d_a) (the frequency set and
+// half-split pairing of the "SpatioTemporal RoPE" section of the HorizonStream
+// post, with three axes).  Angles use the coordinate relative to the volume's
+// origin: every logit depends on coordinate differences only, so this changes no
+// logit and keeps the fp32 angles small.
+//
+// One workgroup per (block, head group, volume).  The block's tokens are gathered
+// from packed order (perm), Q and K are rotated in fp32 and written in canonical
+// order [B, H, N, Dp]; V is written transposed inside the block [B, H, nblk, Dp, |b|]
+// (the layout the attention kernel's P.V contraction reads); the block means of the
+// rotated K (kbar [B, H, nblkp, Dp]) and of V (vbart [B, H, Dp, nblkp]) are summed in
+// a fixed order from LDS, so results are bitwise reproducible and independent of
+// the packing.  HBM bound: reads q, k, v once, writes qrot, krot, vt once.
+#include <cmath>
+
+#include "layout.h"
+
+namespace pack3d {
+namespace {
+
+constexpr int kChunk = 64;  // tokens staged in LDS at a time
+
+__global__ void k_rope_table(float2* tab, int emax, int half, int da, double base) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= emax * half) return;
+  const int c = i / half, k = i - c * half;
+  const double theta = pow(base, -2.0 * (double)k / (double)da);
+  const double phi = (double)c * theta;
+  tab[i] = make_float2((float)cos(phi), (float)sin(phi));
+}
+
+template <typename T, int V>
+struct alignas(sizeof(T) * V) Vec {
+  T v[V];
+};
+
+template <typename T>
+__device__ inline float to_f(T x) { return (float)x; }
+template <typename T>
+__device__ inline T from_f(float x) { return (T)x; }
+
+struct RopeArgs {
+  const void* q; const void* k; const void* v;
+  const int32_t* coords; const int32_t* perm; const int32_t* geom;
+  const float2* tab;
+  void* qrot; void* krot; void* vt; void* kbar; void* vbart;
+  int N, H, D, Dp, nblk, nblkp, bvol, heads_per_group, emax, half;
+};
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
+  extern __shared__ char smem[];
+  const int blk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int N = a.N, H = a.H, D = a.D, Dp = a.Dp, bvol = a.bvol;
+  const int da = D / 3, half = a.half;
+  const int ntok = bvol < kChunk ? bvol : kChunk;
+  const int nchunk = bvol / ntok;
+  // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1] (float), vl[Dp][ntok+8] (T)
+  int* s_src = (int*)smem;
+  int* s_rel = s_src + bvol;
+  float* kl = (float*)(s_rel + 3 * bvol);
+  const int kls = Dp + 1;
+  T* vl = (T*)(kl + ntok * kls);
+  const int vls = ntok + 8;
+
+  const int32_t* g = a.geom + b * G_FIELDS;
+  for (int t = tid; t < bvol; t += 256) {
+    const int kappa = blk * bvol + t;
+    const int src = a.perm[(int64_t)b * N + kappa];
+    s_src[t] = src;
+    const int32_t* c = a.coords + ((int64_t)b * N + src) * 3;
+    for (int ax = 0; ax < 3; ++ax) {
+      int r = c[ax] - g[G_OZ + ax];
+      r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);  // in range whenever coords match the index
+      s_rel[t * 3 + ax] = r;
+    }
+  }
+  __syncthreads();
+
+  const T* q = (const T*)a.q;
+  const T* k = (const T*)a.k;
+  const T* v = (const T*)a.v;
+  T* qrot = (T*)a.qrot;
+  T* krot = (T*)a.krot;
+  T* vt = (T*)a.vt;
+  const int pchunks = half / VEC;         // VEC-wide pieces per half group
+  const int rope_items = ntok * 3 * pchunks;
+  const int v_items = ntok * (D / VEC);
+  const int h0 = hg * a.heads_per_group;
+
+  for (int hh = 0; hh < a.heads_per_group; ++hh) {
+    const int h = h0 + hh;
+    const int64_t bh = (int64_t)b * H + h;
+    float ksum = 0.f, vsum = 0.f;   // column tid < Dp
+    for (int ch = 0; ch < nchunk; ++ch) {
+      const int t0 = ch * ntok;
+      // rotate q and k
+      for (int it = tid; it < rope_items; it += 256) {
+        const int tok = it / (3 * pchunks);
+        const int rem = it - tok * 3 * pchunks;
+        const int ax = rem / pchunks, p = rem - ax * pchunks;
+        const int src = s_src[t0 + tok];
+        const int c = s_rel[(t0 + tok) * 3 + ax];
+        const int col1 = ax * da + p * VEC, col2 = col1 + half;
+        const int64_t in_row = ((int64_t)b * N + src) * H + h;
+        const Vec<T, VEC> q1 = *(const Vec<T, VEC>*)(q + in_row * D + col1);
+        const Vec<T, VEC> q2 = *(const Vec<T, VEC>*)(q + in_row * D + col2);
+        const Vec<T, VEC> k1 = *(const Vec<T, VEC>*)(k + in_row * D + col1);
+        const Vec<T, VEC> k2 = *(const Vec<T, VEC>*)(k + in_row * D + col2);
+        Vec<T, VEC> oq1, oq2, ok1, ok2;
+        const float2* cs = a.tab + (int64_t)c * half + p * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float2 r = cs[e];
+          const float x1 = to_f(q1.v[e]), x2 = to_f(q2.v[e]);
+          oq1.v[e] = from_f<T>(x1 * r.x - x2 * r.y);
+          oq2.v[e] = from_f<T>(x1 * r.y + x2 * r.x);
+          const float y1 = to_f(k1.v[e]), y2 = to_f(k2.v[e]);
+          const float ky1 = y1 * r.x - y2 * r.y;
+          const float ky2 = y1 * r.y + y2 * r.x;
+          ok1.v[e] = from_f<T>(ky1);
+          ok2.v[e] = from_f<T>(ky2);
+          kl[tok * kls + col1 + e] = ky1;
+          kl[tok * kls + col2 + e] = ky2;
+        }
+        const int64_t out_row = (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp;
+        *(Vec<T, VEC>*)(qrot + out_row + col1) = oq1;
+        *(Vec<T, VEC>*)(qrot + out_row + col2) = oq2;
+        *(Vec<T, VEC>*)(krot + out_row + col1) = ok1;
+        *(Vec<T, VEC>*)(krot + out_row + col2) = ok2;
+      }
+      // copy v into the transposed LDS tile
+      for (int it = tid; it < v_items; it += 256) {
+        const int tok = it / (D / VEC);
+        const int col = (it - tok * (D / VEC)) * VEC;
+        const int src = s_src[t0 + tok];
+        const Vec<T, VEC> x = *(const Vec<T, VEC>*)(v + (((int64_t)b * N + src) * H + h) * D + col);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) vl[(col + e) * vls + tok] = x.v[e];
+      }
+      // zero padding columns D..Dp of qrot / krot rows and of the staged tiles
+      if (Dp > D) {
+        const int pad = Dp - D;
+        for (int it = tid; it < ntok * pad; it += 256) {
+          const int tok = it / pad, col = D + it - tok * pad;
+          const int64_t out_row = (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp;
+          qrot[out_row + col] = from_f<T>(0.f);
+          krot[out_row + col] = from_f<T>(0.f);
+          kl[tok * kls + col] = 0.f;
+          vl[col * vls + tok] = from_f<T>(0.f);
+        }
+      }
+      __syncthreads();
+      if (tid < Dp) {
+        float ks = 0.f, vs = 0.f;
+        for (int t = 0; t < ntok; ++t) {
+          ks += kl[t * kls + tid];
+          vs += to_f(vl[tid * vls + t]);
+        }
+        ksum += ks;
+        vsum += vs;
+      }
+      // write V transposed inside the block: vt[bh][blk][d][t0 .. t0+ntok)
+      {
+        const int per_row = ntok / 8;
+        for (int it = tid; it < Dp * per_row; it += 256) {
+          const int d = it / per_row, c8 = (it - d * per_row) * 8;
+          T* dst = vt + ((bh * a.nblk + blk) * Dp + d) * bvol + t0 + c8;
+          const T* srcp = vl + d * vls + c8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dst[e] = srcp[e];
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < Dp) {
+      const float inv = 1.0f / (float)bvol;
+      ((T*)a.kbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(ksum * inv);
+      ((T*)a.vbart)[(bh * Dp + tid) * a.nblkp + blk] = from_f<T>(vsum * inv);
+      // zero the padding summaries nblk .. nblkp (there may be more of them than blocks)
+      for (int pad_blk = a.nblk + blk; pad_blk < a.nblkp; pad_blk += a.nblk) {
+        ((T*)a.kbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
+        ((T*)a.vbart)[(bh * Dp + tid) * a.nblkp + pad_blk] = from_f<T>(0.f);
+      }
+    }
+  }
+}
+
+template <typename T>
+pack3d_status launch_typed(const Dims& d, const RopeArgs& a, hipStream_t s) {
+  const int ntok = d.bvol < kChunk ? d.bvol : kChunk;
+  const size_t lds = sizeof(int) * 4 * d.bvol + sizeof(float) * ntok * (d.Dp + 1) + sizeof(T) * d.Dp * (ntok + 8);
+  dim3 grid(d.nblk, d.H / a.heads_per_group, d.B);
+  ProfileScope prof("rope_pool", s);
+  int vec = 1;
+  const int cap = 16 / (int)sizeof(T);
+  while (vec * 2 <= cap && d.half % (vec * 2) == 0) vec *= 2;
+  switch (vec) {
+    case 1: hipLaunchKernelGGL((k_rope_pool<T, 1>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_rope_pool<T, 2>), grid, dim3(256), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_rope_pool<T, 4>), grid, dim3(256), lds, s, a); break;
+    default:
+      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_rope_pool<T, 8>), grid, dim3(256), lds, s, a);
+      break;
+  }
+  return check_launch("forward: rope/pool");
+}
+
+}  // namespace
+
+pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
+                               const void* q, const void* k, const void* v, const int32_t* coords,
+                               char* ws, const Workspace& w, hipStream_t s) {
+  const int n_tab = d.emax * d.half;
+  {
+  ProfileScope prof("rope_table", s);
+  hipLaunchKernelGGL(k_rope_table, dim3((n_tab + 255) / 256), dim3(256), 0, s,
+                     (float2*)(ws + w.rope), d.emax, d.half, d.D / 3, (double)at->rope_base);
+  }
+  RopeArgs a;
+  a.q = q; a.k = k; a.v = v; a.coords = coords; a.perm = ix->perm; a.geom = ix->geom;
+  a.tab = (const float2*)(ws + w.rope);
+  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vt = ws + w.vt; a.kbar = ws + w.kbar; a.vbart = ws + w.vbart;
+  a.N = d.N; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
+  a.emax = d.emax; a.half = d.half;
+  // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all
+  int hp = d.H;
+  for (int c = 1; c <= d.H; ++c) {
+    if (d.H % c == 0 && ((size_t)c * d.D * d.esize) % 128 == 0) { hp = c; break; }
+  }
+  a.heads_per_group = hp;
+  return at->dtype == PACK3D_BF16 ? launch_typed<bf16>(d, a, s) : launch_typed<float>(d, a, s);
+}
+
+}  // namespace pack3d

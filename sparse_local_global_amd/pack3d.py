@@ -1,0 +1,309 @@
+"""Python binding of libpack3d (the PACK3D C ABI declared in include/pack3d.h).
+
+Argument marshalling only: torch supplies device memory and the stream, every
+step of the operator runs in the library's HIP kernels.  If the library is not
+built, or is loaded without a GPU, calls raise -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpack3d.so")
+
+OK, E_INVALID, E_COORDS, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(6)
+F32, BF16 = 0, 1
+ORDERS = {"any": 0, "raster": 1, "morton": 2, "block": 3, "random": 4}
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class Pack3DError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pack3d status {status}: {message}")
+        self.status = status
+
+
+class Packing(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("tokens_per_volume", ctypes.c_int32), ("order_hint", ctypes.c_int32)]
+
+
+class Attn(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("with_summaries", ctypes.c_int32)]
+
+
+class Tables(ctypes.Structure):
+    _fields_ = [("token_block", ctypes.c_void_p), ("canon", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("nbr", ctypes.c_void_p), ("geom", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("tokens", ctypes.c_int32), ("nblk", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32), ("slots", ctypes.c_int32), ("radius", ctypes.c_int32),
+                ("block_shape", ctypes.c_int32 * 3), ("extent_max", ctypes.c_int32 * 3)]
+
+
+class Views(ctypes.Structure):
+    _fields_ = [("rope_table", ctypes.c_size_t), ("qrot", ctypes.c_size_t), ("krot", ctypes.c_size_t),
+                ("vt", ctypes.c_size_t), ("kbar", ctypes.c_size_t), ("vbart", ctypes.c_size_t),
+                ("head_dim_padded", ctypes.c_int32), ("nblk_padded", ctypes.c_int32),
+                ("extent_table", ctypes.c_int32)]
+
+
+EXPORTS = {
+    "pack3d_index_bytes": (ctypes.c_size_t, [ctypes.POINTER(Packing), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
+    "pack3d_build_index": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Packing), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_void_p)]),
+    "pack3d_index_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Tables)]),
+    "pack3d_index_geometry": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+    "pack3d_index_free": (None, [ctypes.c_void_p]),
+    "pack3d_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.POINTER(Attn), ctypes.c_int]),
+    "pack3d_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 6
+                       + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pack3d_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 10
+                        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pack3d_workspace_views": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn), ctypes.POINTER(Views)]),
+    "pack3d_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
+    "pack3d_profile_read": (ctypes.c_int32, [ctypes.c_char_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
+                                             ctypes.POINTER(ctypes.c_double), ctypes.c_int32]),
+    "pack3d_profile_reset": (None, []),
+    "pack3d_last_error": (ctypes.c_char_p, []),
+    "pack3d_version": (ctypes.c_int32, []),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpack3d.so (after torch, so the process holds a single HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise Pack3DError(E_INVALID, f"{path} is not built (run __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        raise Pack3DError(status, load_library().pack3d_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class Index:
+    """A built PACK3D index: the device tables (owned here) plus the library handle."""
+
+    def __init__(self, handle, tables: torch.Tensor, batch, tokens, block_shape, radius):
+        self._handle = handle
+        self.tables_buffer = tables
+        self.batch, self.tokens = batch, tokens
+        self.block_shape, self.radius = tuple(block_shape), radius
+
+    @property
+    def handle(self):
+        if self._handle is None:
+            raise Pack3DError(E_INVALID, "index has been freed")
+        return self._handle
+
+    def free(self):
+        if self._handle is not None:
+            load_library().pack3d_index_free(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def _view(self, ptr, count):
+        base = self.tables_buffer.data_ptr()
+        off = ptr - base
+        return self.tables_buffer[off: off + 4 * count].view(torch.int32)
+
+    def tables(self) -> dict:
+        t = Tables()
+        _check(load_library().pack3d_index_tables(self.handle, ctypes.byref(t)))
+        b, n, nblk, slots = t.batch, t.tokens, t.nblk, t.slots
+        return dict(token_block=self._view(t.token_block, b * n).view(b, n),
+                    canon=self._view(t.canon, b * n).view(b, n),
+                    perm=self._view(t.perm, b * n).view(b, n),
+                    nbr=self._view(t.nbr, b * nblk * slots).view(b, nblk, slots),
+                    geom=self._view(t.geom, b * 8).view(b, 8),
+                    nblk=nblk, block_tokens=t.block_tokens, slots=slots,
+                    extent_max=tuple(t.extent_max))
+
+    def geometry(self, volume: int):
+        out = (ctypes.c_int32 * 6)()
+        _check(load_library().pack3d_index_geometry(self.handle, volume, out))
+        return tuple(out[:3]), tuple(out[3:])
+
+
+def index_bytes(batch, tokens, block_shape, radius) -> int:
+    p = Packing(batch, tokens, 0)
+    bs = (ctypes.c_int32 * 3)(*block_shape)
+    return load_library().pack3d_index_bytes(ctypes.byref(p), bs, radius)
+
+
+def build_index(coords: torch.Tensor, block_shape, local_radius: int, order_hint: str = "any") -> Index:
+    """coords: int32 [B, N, 3] (z, y, x) on the GPU."""
+    lib = load_library()
+    if coords.dtype != torch.int32 or coords.dim() != 3 or coords.shape[-1] != 3 or not coords.is_cuda:
+        raise Pack3DError(E_INVALID, "coords must be a CUDA int32 tensor [B, N, 3]")
+    coords = coords.contiguous()
+    b, n = coords.shape[0], coords.shape[1]
+    p = Packing(b, n, ORDERS.get(order_hint, 0))
+    bs = (ctypes.c_int32 * 3)(*block_shape)
+    nbytes = lib.pack3d_index_bytes(ctypes.byref(p), bs, local_radius)
+    tables = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=coords.device)
+    handle = ctypes.c_void_p()
+    _check(lib.pack3d_build_index(_ptr(coords), ctypes.byref(p), bs, local_radius, _ptr(tables),
+                                  nbytes, ctypes.c_void_p(_stream()), ctypes.byref(handle)))
+    return Index(handle, tables, b, n, block_shape, local_radius)
+
+
+def make_attn(dtype, heads, head_dim, rope_base=10000.0, scale=None, with_summaries=True) -> Attn:
+    if dtype not in _DTYPES:
+        raise Pack3DError(E_UNSUPPORTED, f"dtype {dtype} is not supported")
+    return Attn(_DTYPES[dtype], heads, head_dim, float(rope_base), 0.0 if scale is None else float(scale),
+                1 if with_summaries else 0)
+
+
+def workspace_bytes(index: Index, attn: Attn, for_backward: bool = False) -> int:
+    return load_library().pack3d_workspace_bytes(index.handle, ctypes.byref(attn), 1 if for_backward else 0)
+
+
+def _check_act(name, t, shape, dtype):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda or not t.is_contiguous():
+        raise Pack3DError(E_INVALID, f"{name} must be a contiguous CUDA {dtype} tensor of shape {tuple(shape)}")
+
+
+def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, with_summaries=True,
+            workspace: torch.Tensor | None = None, out=None, lse=None):
+    """PACK3D forward.  q, k, v [B, N, H, D]; returns (out [B, N, H, D], lse fp32 [B, H, N])."""
+    lib = load_library()
+    b, n, h, d = q.shape
+    attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_act(name, t, (b, n, h, d), q.dtype)
+    need = workspace_bytes(index, attn)
+    if need == 0:
+        raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    _check(lib.pack3d_forward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(coords.contiguous()),
+                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                              ctypes.c_void_p(_stream())))
+    return out, lse
+
+
+def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0, scale=None,
+             with_summaries=True, workspace: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv) of sum(out * dout) with respect to the unrotated q, k, v."""
+    lib = load_library()
+    b, n, h, d = q.shape
+    attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_act(name, t, (b, n, h, d), q.dtype)
+    need = workspace_bytes(index, attn, True)
+    if need == 0:
+        raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.pack3d_backward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(coords.contiguous()), _ptr(out), _ptr(lse.contiguous()), _ptr(dout.contiguous()),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                               ctypes.c_void_p(_stream())))
+    return dq, dk, dv
+
+
+def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_base=10000.0) -> dict:
+    """Tensor views of the forward intermediates left in ``workspace``."""
+    b, n, h, d = q_shape
+    attn = make_attn(dtype, h, d, rope_base)
+    vw = Views()
+    _check(load_library().pack3d_workspace_views(index.handle, ctypes.byref(attn), ctypes.byref(vw)))
+    dp, nbp = vw.head_dim_padded, vw.nblk_padded
+    es = 2 if dtype == torch.bfloat16 else 4
+    tab = index.tables()
+    nblk, bvol = tab["nblk"], tab["block_tokens"]
+
+    def view(off, shape, dt=dtype, esize=es):
+        cnt = math.prod(shape)
+        return workspace[off: off + cnt * esize].view(dt).view(*shape)
+
+    half = d // 6
+    return dict(rope_table=view(vw.rope_table, (vw.extent_table, half, 2), torch.float32, 4),
+                qrot=view(vw.qrot, (b, h, n, dp)), krot=view(vw.krot, (b, h, n, dp)),
+                vt=view(vw.vt, (b, h, nblk, dp, bvol)), kbar=view(vw.kbar, (b, h, nbp, dp)),
+                vbart=view(vw.vbart, (b, h, dp, nbp)))
+
+
+def profile_enable(enable: bool = True):
+    """Bracket every library kernel launch with HIP events on its stream (see profile_read)."""
+    _check(load_library().pack3d_profile_enable(1 if enable else 0))
+
+
+def profile_reset():
+    load_library().pack3d_profile_reset()
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} since the last reset (waits for the events)."""
+    n_max = 32
+    names = ctypes.create_string_buffer(48 * n_max)
+    launches = (ctypes.c_int32 * n_max)()
+    ms = (ctypes.c_double * n_max)()
+    n = load_library().pack3d_profile_read(names, len(names), launches, ms, n_max)
+    if n < 0:
+        raise Pack3DError(E_HIP, "profile_read: HIP event error")
+    out, parts = {}, names.raw.split(b"\0")
+    for i in range(n):
+        out[parts[i].decode()] = (launches[i], ms[i])
+    return out
+
+
+class Pack3DAttention(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in libpack3d."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True):
+        out, lse = forward(index, q.contiguous(), k.contiguous(), v.contiguous(), coords, rope_base=rope_base,
+                           scale=scale, with_summaries=with_summaries)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.index, ctx.coords = index, coords
+        ctx.opts = (rope_base, scale, with_summaries)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        rope_base, scale, with_summaries = ctx.opts
+        dq, dk, dv = backward(ctx.index, q, k, v, ctx.coords, out, lse, dout.contiguous(), rope_base=rope_base,
+                              scale=scale, with_summaries=with_summaries)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def attention(q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True):
+    """PACK3D attention with autograd support."""
+    return Pack3DAttention.apply(q, k, v, index, coords, rope_base, scale, with_summaries)

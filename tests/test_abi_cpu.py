@@ -1,0 +1,94 @@
+"""The C-ABI library builds, loads and exports every entry point declared in include/pack3d.h.
+
+Host-side checks only: no call here reaches a GPU (argument errors are rejected
+before any HIP call).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_local_global_amd.pack3d as p3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pack3d.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pack3d_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = p3.load_library()
+    names = _declared_functions()
+    assert len(names) == 14
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) <= set(p3.EXPORTS)
+
+
+def test_exported_symbols_in_dynamic_table():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", p3.LIB_PATH], capture_output=True, text=True).stdout
+    for name in _declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_last_error():
+    lib = p3.load_library()
+    assert lib.pack3d_version() == 100
+    assert isinstance(lib.pack3d_last_error(), bytes)
+
+
+def test_index_bytes_depends_only_on_layout():
+    assert p3.index_bytes(2, 65536, (4, 4, 4), 1) > 0
+    nblk, slots = 1024, 27
+    expect = 0
+    for count in (2 * 8, 2 * 65536, 2 * 65536, 2 * 65536, 2 * nblk * slots):
+        expect = (expect + 4 * count + 255) // 256 * 256
+    assert p3.index_bytes(2, 65536, (4, 4, 4), 1) == expect
+    assert p3.index_bytes(1, 100, (4, 4, 4), 1) == 0      # 100 tokens cannot tile into 64-token blocks
+    assert p3.index_bytes(1, 512, (2, 2, 2), -1) == 0
+    assert p3.index_bytes(1, 512, (0, 2, 2), 1) == 0
+    assert p3.index_bytes(0, 512, (2, 2, 2), 1) == 0
+
+
+def test_build_index_argument_errors_return_codes():
+    lib = p3.load_library()
+    pk = p3.Packing(1, 512, 0)
+    bs = (ctypes.c_int32 * 3)(2, 2, 2)
+    h = ctypes.c_void_p()
+    st = lib.pack3d_build_index(None, ctypes.byref(pk), bs, 1, ctypes.c_void_p(256), 1 << 20, None, ctypes.byref(h))
+    assert st == p3.E_INVALID and b"null" in lib.pack3d_last_error()
+    st = lib.pack3d_build_index(ctypes.c_void_p(256), ctypes.byref(pk), bs, -1, ctypes.c_void_p(256), 1 << 20,
+                                None, ctypes.byref(h))
+    assert st == p3.E_INVALID
+    st = lib.pack3d_build_index(ctypes.c_void_p(256), ctypes.byref(pk), bs, 9, ctypes.c_void_p(256), 1 << 20,
+                                None, ctypes.byref(h))
+    assert st == p3.E_UNSUPPORTED
+    pk2 = p3.Packing(1, 500, 0)
+    st = lib.pack3d_build_index(ctypes.c_void_p(256), ctypes.byref(pk2), bs, 1, ctypes.c_void_p(256), 1 << 20,
+                                None, ctypes.byref(h))
+    assert st == p3.E_COORDS
+    bs3 = (ctypes.c_int32 * 3)(1, 1, 3)                      # 3-token blocks: not a multiple of 8
+    pk3 = p3.Packing(1, 48, 0)
+    st = lib.pack3d_build_index(ctypes.c_void_p(256), ctypes.byref(pk3), bs3, 1, ctypes.c_void_p(256), 1 << 20,
+                                None, ctypes.byref(h))
+    assert st == p3.E_UNSUPPORTED
+    st = lib.pack3d_build_index(ctypes.c_void_p(256), ctypes.byref(pk), bs, 1, ctypes.c_void_p(256), 16,
+                                None, ctypes.byref(h))
+    assert st == p3.E_WORKSPACE
+    assert not h.value
+
+
+def test_forward_argument_errors_return_codes():
+    lib = p3.load_library()
+    at = p3.Attn(p3.BF16, 8, 96, 10000.0, 0.0, 1)
+    st = lib.pack3d_forward(None, ctypes.byref(at), *([None] * 6), None, 0, None)
+    assert st == p3.E_INVALID
+    assert lib.pack3d_workspace_bytes(None, ctypes.byref(at), 0) == 0
+    st = lib.pack3d_backward(None, ctypes.byref(at), *([None] * 10), None, 0, None)
+    assert st == p3.E_INVALID
