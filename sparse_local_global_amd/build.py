@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpack3d.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "index.hip", "profile.hip", "rope_pool.hip", "attn_fwd.hip"]
+SOURCES = ["api.hip", "index.hip", "profile.hip", "rope_pool.hip", "attn_fwd.hip", "attn_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -91,7 +91,7 @@ extern "C" pack3d_status pack3d_forward(const pack3d_index* ix, const pack3d_att
   if (ws_bytes < w.fwd_total)
     return set_error(PACK3D_E_WORKSPACE, "forward: workspace %zu bytes < %zu needed", ws_bytes, w.fwd_total);
   hipStream_t s = (hipStream_t)stream;
-  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, s);
+  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, false, s);
   if (st != PACK3D_OK) return st;
   return launch_attn_fwd(d, ix, at, (const char*)ws, w, out, lse, s);
 }
@@ -102,7 +102,17 @@ extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_at
                                          void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
   pack3d_status st = check_attn(ix, at, "backward");
   if (st != PACK3D_OK) return st;
-  (void)q; (void)k; (void)v; (void)coords; (void)out; (void)lse; (void)dout; (void)dq; (void)dk; (void)dv;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return set_error(PACK3D_E_UNSUPPORTED, "backward: not built yet");
+  if (!q || !k || !v || !coords || !out || !lse || !dout || !dq || !dk || !dv || !ws)
+    return set_error(PACK3D_E_INVALID, "backward: null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(ws))
+    return set_error(PACK3D_E_INVALID, "backward: q, k, v, out, dout and workspace must be 16-byte aligned");
+  Dims d = make_dims(ix, at);
+  Workspace w = workspace_layout(d);
+  if (ws_bytes < w.bwd_total)
+    return set_error(PACK3D_E_WORKSPACE, "backward: workspace %zu bytes < %zu needed", ws_bytes, w.bwd_total);
+  hipStream_t s = (hipStream_t)stream;
+  // recompute the rotated / pooled operands in every layout the gradient kernels read
+  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, true, s);
+  if (st != PACK3D_OK) return st;
+  return launch_attn_bwd(d, ix, at, coords, out, lse, dout, dq, dk, dv, (char*)ws, w, s);
 }

@@ -1,0 +1,559 @@
+// PACK3D backward: gradients of sum(out * dout) with respect to the unrotated q, k, v,
+// through the shared softmax, the block mean pooling and the axial RoPE.
+//
+// "Geometry Matters in Packed 3D Attention" (abstract) presents the operator as
+// trainable at scale; the gradients follow from its definition.  With
+// P = exp(logit - lse) for local keys j and summaries b of query i,
+//   delta_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, V_j> - delta_i),  dT_ib = P_ib (<dO_i, Vbar_b> - delta_i)
+//   dQ~_i   = scale (sum_j dS_ij K~_j + sum_b dT_ib Kbar_b)
+//   dK~_j   = scale sum_i dS_ij Q~_i + dKbar_b(j) / |b|,  dKbar_b = scale sum_i dT_ib Q~_i
+//   dV_j    = sum_i P_ij dO_i + dVbar_b(j) / |b|,         dVbar_b = sum_i P_ib dO_i
+//   dq = R(c)^T dQ~, dk = R(c)^T dK~  (R orthogonal; the mean broadcasts 1/|b| to each member).
+//
+// Kernels, in launch order (no atomics anywhere, so results are bitwise reproducible):
+//   bwd_pre      per block: delta, dO gathered to canonical order (row-major and transposed
+//                inside the block), lse gathered to canonical order
+//   bwd_summary  summary-major: each workgroup owns 64 summaries of one (volume, head) and a
+//                chunk of query blocks; masks the summaries local to each query block and
+//                accumulates partial dKbar, dVbar (fp32) per chunk
+//   bwd_reduce   sums the chunks in a fixed order
+//   bwd_local    key-major: each workgroup owns 64 keys and walks the query tiles of their
+//                neighbour blocks (the neighbourhood is symmetric) for dK~, dV; the epilogue
+//                adds the broadcast summary gradients, applies R^T and scatters dk, dv to
+//                packed order
+//   bwd_dq       query-major (like the forward, recomputing P from lse): dQ~ over local and
+//                summary tiles; the epilogue applies R^T and scatters dq
+// The waves hold their 16 columns (keys, summaries or queries) in registers and stream
+// 64-row tiles through LDS; the two contraction shapes are the ones of tiles.h.
+#include <cmath>
+
+#include "tiles.h"
+
+namespace pack3d {
+namespace {
+
+struct BwdArgs {
+  // forward intermediates and backward layouts (workspace, canonical order)
+  const void* qrot; const void* krot; const void* qt; const void* kt; const void* vr;
+  const void* kbar; const void* kbart; const void* vbar;
+  void* doc; void* dot; float* lsec; float* delta;
+  float* dkbar; float* dvbar; float* part_k; float* part_v;
+  const float2* tab;
+  // caller buffers (packed order)
+  const void* out; const float* lse; const void* dout;
+  void* dq; void* dk; void* dv;
+  const int32_t* coords; const int32_t* perm; const int32_t* nbr; const int32_t* geom;
+  int B, N, H, D, Dp, nblk, nblkp, bvol, slots, radius, tiles_per_block, with_summaries, chunks, half, emax;
+  int bz, by, bx;
+  float scale, scale_log2;
+};
+
+template <typename T, int V>
+struct alignas(sizeof(T) * V) Vec {
+  T v[V];
+};
+
+// ---------------------------------------------------------------------------------
+// bwd_pre: one workgroup per (block, head, volume)
+// ---------------------------------------------------------------------------------
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
+  extern __shared__ char smem[];
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int N = a.N, D = a.D, Dp = a.Dp, bvol = a.bvol;
+  const int ntok = bvol < kTile ? bvol : kTile;
+  const int nch = D / VEC;
+  float* part = (float*)smem;                          // [ntok][nch]
+  T* dl = (T*)(part + ntok * nch);                     // [Dp][ntok + 8]
+  const int dls = ntok + 8;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const T* dout = (const T*)a.dout;
+  const T* out = (const T*)a.out;
+  T* doc = (T*)a.doc;
+  for (int t0 = 0; t0 < bvol; t0 += ntok) {
+    for (int it = tid; it < ntok * nch; it += 256) {
+      const int tok = it / nch, c = (it - tok * nch) * VEC;
+      const int kappa = blk * bvol + t0 + tok;
+      const int src = a.perm[(int64_t)b * N + kappa];
+      const int64_t in = (((int64_t)b * N + src) * a.H + h) * D + c;
+      const Vec<T, VEC> g = *(const Vec<T, VEC>*)(dout + in);
+      const Vec<T, VEC> o = *(const Vec<T, VEC>*)(out + in);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        acc += (float)g.v[e] * (float)o.v[e];
+        dl[(c + e) * dls + tok] = g.v[e];
+      }
+      part[it] = acc;   // it = tok * nch + chunk index
+      *(Vec<T, VEC>*)(doc + (bh * N + kappa) * Dp + c) = g;
+    }
+    if (Dp > D) {
+      const int pad = Dp - D;
+      for (int it = tid; it < ntok * pad; it += 256) {
+        const int tok = it / pad, c = D + it - tok * pad;
+        doc[(bh * N + blk * bvol + t0 + tok) * Dp + c] = (T)0.f;
+        dl[c * dls + tok] = (T)0.f;
+      }
+    }
+    __syncthreads();
+    if (tid < ntok) {
+      const int kappa = blk * bvol + t0 + tid;
+      const int src = a.perm[(int64_t)b * N + kappa];
+      float s = 0.f;
+      for (int c = 0; c < nch; ++c) s += part[tid * nch + c];
+      a.delta[bh * N + kappa] = s;
+      a.lsec[bh * N + kappa] = a.lse[bh * N + src];
+    }
+    const int per_row = ntok / 8;
+    for (int it = tid; it < Dp * per_row; it += 256) {
+      const int d = it / per_row, c8 = (it - d * per_row) * 8;
+      T* dst = (T*)a.dot + ((bh * a.nblk + blk) * Dp + d) * bvol + t0 + c8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = dl[d * dls + c8 + e];
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Epilogue shared by bwd_local and bwd_dq: rows of fp32 gradients staged in LDS
+// (canonical rows row0 .. row0+nrows), optionally rotated back by R^T, written in
+// the output dtype to packed order.
+// ---------------------------------------------------------------------------------
+template <typename T>
+__device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, int nrows, int b, int h, int row0,
+                                  bool unrotate, T* dst, int* s_src, int* s_rel) {
+  const int tid = threadIdx.x;
+  const int N = a.N, D = a.D;
+  if (tid < nrows) {
+    const int src = a.perm[(int64_t)b * N + row0 + tid];
+    s_src[tid] = src;
+    const int32_t* g = a.geom + b * G_FIELDS;
+    const int32_t* c = a.coords + ((int64_t)b * N + src) * 3;
+    for (int ax = 0; ax < 3; ++ax) {
+      int r = c[ax] - g[G_OZ + ax];
+      r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);
+      s_rel[tid * 3 + ax] = r;
+    }
+  }
+  __syncthreads();
+  const int da = D / 3, half = a.half;
+  for (int it = tid; it < nrows * D; it += kThreads) {
+    const int r = it / D, col = it - r * D;
+    float v = st[r * sts + col];
+    if (unrotate) {
+      const int ax = col / da, k = col - ax * da;
+      const int kk = k < half ? k : k - half;
+      const float2 cs = a.tab[(int64_t)s_rel[r * 3 + ax] * half + kk];
+      if (k < half) v = v * cs.x + st[r * sts + col + half] * cs.y;      // y1 c + y2 s
+      else v = -st[r * sts + col - half] * cs.y + v * cs.x;              // -y1 s + y2 c
+    }
+    dst[(((int64_t)b * N + s_src[r]) * a.H + h) * D + col] = (T)v;
+  }
+  __syncthreads();  // s_src / s_rel are rewritten by the next call
+}
+
+// ---------------------------------------------------------------------------------
+// bwd_summary: workgroup = (64 summaries, head, volume x query chunk)
+// ---------------------------------------------------------------------------------
+template <typename T, int DP>
+struct SumSmem {
+  RowTile<T, DP> q, g;
+  TrTile<T, DP> qt, gt;
+  float lse[kTile], delta[kTile];
+};
+
+template <typename T, int DP>
+__global__ __launch_bounds__(kThreads) void k_bwd_summary(BwdArgs a) {
+  __shared__ SumSmem<T, DP> sm;
+  const int r0 = blockIdx.x * kTile, h = blockIdx.y;
+  const int b = blockIdx.z / a.chunks, chunk = blockIdx.z - b * a.chunks;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int N = a.N, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int sid = r0 + 16 * wave + col;          // this lane's summary (block id)
+  ColFrag<T, DP> kf, vf;
+  kf.load((const T*)a.kbar + (bh * a.nblkp + sid) * DP, true, grp);   // padding rows are zero
+  vf.load((const T*)a.vbar + (bh * a.nblkp + sid) * DP, true, grp);
+  const int32_t* g = a.geom + b * G_FIELDS;
+  const int nby = g[G_EY] / a.by, nbx = g[G_EX] / a.bx;
+  const int sz = sid / (nby * nbx), sy = (sid / nbx) % nby, sx = sid % nbx;
+  f32x4 dk[DP / 16], dv[DP / 16];
+#pragma unroll
+  for (int dt = 0; dt < DP / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int q_begin = (int)((int64_t)chunk * a.nblk / a.chunks);
+  const int q_end = (int)((int64_t)(chunk + 1) * a.nblk / a.chunks);
+  const int nrow = bvol < kTile ? bvol : kTile;
+  const T* qrot = (const T*)a.qrot + bh * N * DP;
+  const T* doc = (const T*)a.doc + bh * N * DP;
+  const T* qt = (const T*)a.qt + bh * a.nblk * DP * bvol;
+  const T* dot = (const T*)a.dot + bh * a.nblk * DP * bvol;
+  for (int qb = q_begin; qb < q_end; ++qb) {
+    const int qz = qb / (nby * nbx), qy = (qb / nbx) % nby, qx = qb % nbx;
+    const int cheb = max(max(abs(qz - sz), abs(qy - sy)), abs(qx - sx));
+    const bool masked = sid >= a.nblk || cheb <= a.radius;
+    for (int qs = 0; qs < a.tiles_per_block; ++qs) {
+      const int row0 = qb * bvol + qs * kTile;
+      load_rows(sm.q, qrot, nrow, [&](int r) -> int64_t { return (int64_t)(row0 + r) * DP; });
+      load_rows(sm.g, doc, nrow, [&](int r) -> int64_t { return (int64_t)(row0 + r) * DP; });
+      load_tr(sm.qt, qt, nrow, [&](int d, int r) -> int64_t { return ((int64_t)qb * DP + d) * bvol + qs * kTile + r; });
+      load_tr(sm.gt, dot, nrow, [&](int d, int r) -> int64_t { return ((int64_t)qb * DP + d) * bvol + qs * kTile + r; });
+      if (tid < kTile) {
+        sm.lse[tid] = tid < nrow ? a.lsec[bh * N + row0 + tid] : INFINITY;
+        sm.delta[tid] = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
+      }
+      __syncthreads();
+      f32x4 s[4], dp[4];
+      score(sm.q, kf, s, col, grp);
+      score(sm.g, vf, dp, col, grp);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * grp + i;
+          const float p = masked ? 0.f : exp2f(s[mt][i] * a.scale_log2 - sm.lse[r] * kLog2e);
+          s[mt][i] = p;
+          dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
+        }
+      }
+      accum(sm.gt, s, dv, col, grp);
+      accum(sm.qt, dp, dk, col, grp);
+      __syncthreads();
+    }
+  }
+  const int64_t base = (((int64_t)chunk * a.B * a.H + bh) * a.nblkp + sid) * DP;
+#pragma unroll
+  for (int dt = 0; dt < DP / 16; ++dt) {
+    *(f32x4*)(a.part_k + base + 16 * dt + 4 * grp) = dk[dt] * a.scale;
+    *(f32x4*)(a.part_v + base + 16 * dt + 4 * grp) = dv[dt];
+  }
+}
+
+__global__ void k_bwd_reduce(const float* __restrict__ pk, const float* __restrict__ pv, float* dk, float* dv,
+                             int64_t n, int chunks) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float sk = 0.f, sv = 0.f;
+  for (int c = 0; c < chunks; ++c) {
+    sk += pk[c * n + i];
+    sv += pv[c * n + i];
+  }
+  dk[i] = sk;
+  dv[i] = sv;
+}
+
+// ---------------------------------------------------------------------------------
+// bwd_local: workgroup = (64 keys of one block, head, volume)
+// ---------------------------------------------------------------------------------
+template <typename T, int DP>
+struct LocSmem {
+  union {
+    struct {
+      RowTile<T, DP> q, g;
+      TrTile<T, DP> qt, gt;
+    } t;
+    float st[2][kTile][DP + 1];
+  } u;
+  float lse[kTile], delta[kTile];
+  int list[kMaxSlots];
+  int nloc;
+  int src[kTile], rel[kTile * 3];
+};
+
+template <typename T, int DP>
+__global__ __launch_bounds__(kThreads) void k_bwd_local(BwdArgs a) {
+  __shared__ LocSmem<T, DP> sm;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int kb = tile / a.tiles_per_block, ks = tile - kb * a.tiles_per_block;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int N = a.N, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int nk = bvol < kTile ? bvol : kTile;
+  const int krow0 = kb * bvol + ks * kTile;
+  const int kloc = 16 * wave + col;
+  ColFrag<T, DP> kf, vf;
+  kf.load((const T*)a.krot + (bh * N + krow0 + kloc) * DP, kloc < nk, grp);
+  vf.load((const T*)a.vr + (bh * N + krow0 + kloc) * DP, kloc < nk, grp);
+  if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + kb) * a.slots, a.slots, sm.list, &sm.nloc);
+  __syncthreads();
+  const int nloc = sm.nloc;
+  f32x4 dk[DP / 16], dv[DP / 16];
+#pragma unroll
+  for (int dt = 0; dt < DP / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const T* qrot = (const T*)a.qrot + bh * N * DP;
+  const T* doc = (const T*)a.doc + bh * N * DP;
+  const T* qt = (const T*)a.qt + bh * a.nblk * DP * bvol;
+  const T* dot = (const T*)a.dot + bh * a.nblk * DP * bvol;
+  const int nq = nloc * bvol;
+  const int ntiles = (nq + kTile - 1) / kTile;
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kTile;
+    const int valid = nq - j0 < kTile ? nq - j0 : kTile;
+    auto rowoff = [&](int r) -> int64_t {
+      const int j = j0 + r, blk = sm.list[j / bvol];
+      return ((int64_t)blk * bvol + (j - (j / bvol) * bvol)) * DP;
+    };
+    auto troff = [&](int d, int r) -> int64_t {
+      const int j = j0 + r, blk = sm.list[j / bvol];
+      return ((int64_t)blk * DP + d) * bvol + (j - (j / bvol) * bvol);
+    };
+    load_rows(sm.u.t.q, qrot, valid, rowoff);
+    load_rows(sm.u.t.g, doc, valid, rowoff);
+    load_tr(sm.u.t.qt, qt, valid, troff);
+    load_tr(sm.u.t.gt, dot, valid, troff);
+    if (tid < kTile) {
+      const int j = j0 + tid;
+      float l = INFINITY, dl = 0.f;
+      if (tid < valid) {
+        const int blk = sm.list[j / bvol];
+        const int64_t row = (int64_t)blk * bvol + (j - (j / bvol) * bvol);
+        l = a.lsec[bh * N + row];
+        dl = a.delta[bh * N + row];
+      }
+      sm.lse[tid] = l;
+      sm.delta[tid] = dl;
+    }
+    __syncthreads();
+    f32x4 s[4], dp[4];
+    score(sm.u.t.q, kf, s, col, grp);
+    score(sm.u.t.g, vf, dp, col, grp);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * grp + i;
+        const float p = exp2f(s[mt][i] * a.scale_log2 - sm.lse[r] * kLog2e);   // lse = +inf -> 0
+        s[mt][i] = p;
+        dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
+      }
+    }
+    accum(sm.u.t.gt, s, dv, col, grp);
+    accum(sm.u.t.qt, dp, dk, col, grp);
+    __syncthreads();
+  }
+
+  // epilogue: dK~ = scale * acc + dKbar / |b|, dV = acc + dVbar / |b|; then R^T and scatter
+  const float inv = 1.0f / (float)bvol;
+  const float* dkb = a.dkbar + (bh * a.nblkp + kb) * DP;
+  const float* dvb = a.dvbar + (bh * a.nblkp + kb) * DP;
+#pragma unroll
+  for (int dt = 0; dt < DP / 16; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * dt + 4 * grp + i;
+      float xk = dk[dt][i] * a.scale, xv = dv[dt][i];
+      if (a.with_summaries) {
+        xk += dkb[d] * inv;
+        xv += dvb[d] * inv;
+      }
+      sm.u.st[0][kloc][d] = xk;
+      sm.u.st[1][kloc][d] = xv;
+    }
+  }
+  __syncthreads();
+  write_rows<T>(a, &sm.u.st[0][0][0], DP + 1, nk, b, h, krow0, true, (T*)a.dk, sm.src, sm.rel);
+  write_rows<T>(a, &sm.u.st[1][0][0], DP + 1, nk, b, h, krow0, false, (T*)a.dv, sm.src, sm.rel);
+}
+
+// ---------------------------------------------------------------------------------
+// bwd_dq: workgroup = (64 queries of one block, head, volume)
+// ---------------------------------------------------------------------------------
+template <typename T, int DP>
+struct DqSmem {
+  union {
+    struct {
+      RowTile<T, DP> k, v;
+      TrTile<T, DP> kt;
+    } t;
+    float st[kTile][DP + 1];
+  } u;
+  int list[kMaxSlots];
+  uint32_t mask[kMaxBlocks / 32];
+  int nloc;
+  int src[kTile], rel[kTile * 3];
+};
+
+template <typename T, int DP, typename Valid>
+__device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf, const ColFrag<T, DP>& gf,
+                               f32x4 (&dq)[DP / 16], float lse2, float delta, float scale_log2, int col, int grp,
+                               Valid valid) {
+  f32x4 s[4], dp[4];
+  score(sm.u.t.k, qf, s, col, grp);
+  score(sm.u.t.v, gf, dp, col, grp);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = valid(16 * mt + 4 * grp + i) ? exp2f(s[mt][i] * scale_log2 - lse2) : 0.f;
+      dp[mt][i] = p * (dp[mt][i] - delta);
+    }
+  }
+  accum(sm.u.t.kt, dp, dq, col, grp);
+}
+
+template <typename T, int DP>
+__global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
+  __shared__ DqSmem<T, DP> sm;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int qb = tile / a.tiles_per_block, qs = tile - qb * a.tiles_per_block;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int N = a.N, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int nq = bvol < kTile ? bvol : kTile;
+  const int qrow0 = qb * bvol + qs * kTile;
+  const int qloc = 16 * wave + col;
+  const bool qok = qloc < nq;
+  ColFrag<T, DP> qf, gf;
+  qf.load((const T*)a.qrot + (bh * N + qrow0 + qloc) * DP, qok, grp);
+  gf.load((const T*)a.doc + (bh * N + qrow0 + qloc) * DP, qok, grp);
+  const float lse2 = qok ? a.lsec[bh * N + qrow0 + qloc] * kLog2e : INFINITY;
+  const float delta = qok ? a.delta[bh * N + qrow0 + qloc] : 0.f;
+
+  const int mask_words = a.nblkp / 32;
+  for (int i = tid; i < mask_words; i += kThreads) sm.mask[i] = 0u;
+  if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
+  __syncthreads();
+  const int nloc = sm.nloc;
+  for (int i = tid; i < nloc; i += kThreads) atomicOr(&sm.mask[sm.list[i] >> 5], 1u << (sm.list[i] & 31));
+  f32x4 dq[DP / 16];
+#pragma unroll
+  for (int dt = 0; dt < DP / 16; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const T* krot = (const T*)a.krot + bh * N * DP;
+  const T* vr = (const T*)a.vr + bh * N * DP;
+  const T* kt = (const T*)a.kt + bh * a.nblk * DP * bvol;
+  const int nkeys = nloc * bvol;
+  const int ntiles = (nkeys + kTile - 1) / kTile;
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kTile;
+    const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
+    auto rowoff = [&](int r) -> int64_t {
+      const int j = j0 + r, blk = sm.list[j / bvol];
+      return ((int64_t)blk * bvol + (j - (j / bvol) * bvol)) * DP;
+    };
+    load_rows(sm.u.t.k, krot, valid, rowoff);
+    load_rows(sm.u.t.v, vr, valid, rowoff);
+    load_tr(sm.u.t.kt, kt, valid, [&](int d, int r) -> int64_t {
+      const int j = j0 + r, blk = sm.list[j / bvol];
+      return ((int64_t)blk * DP + d) * bvol + (j - (j / bvol) * bvol);
+    });
+    __syncthreads();
+    dq_step<T, DP>(sm, qf, gf, dq, lse2, delta, a.scale_log2, col, grp, [&](int r) { return r < valid; });
+    __syncthreads();
+  }
+  if (a.with_summaries) {
+    const T* kbar = (const T*)a.kbar + bh * a.nblkp * DP;
+    const T* vbar = (const T*)a.vbar + bh * a.nblkp * DP;
+    const T* kbart = (const T*)a.kbart + bh * DP * a.nblkp;
+    const int nst = a.nblkp / kTile;
+    for (int t = 0; t < nst; ++t) {
+      const int r0 = t * kTile;
+      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
+      const uint64_t used = ((uint64_t)sm.mask[2 * t + 1] << 32) | sm.mask[2 * t];
+      const uint64_t live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
+      if (live == 0ull) continue;
+      load_rows(sm.u.t.k, kbar, kTile, [&](int r) -> int64_t { return (int64_t)(r0 + r) * DP; });
+      load_rows(sm.u.t.v, vbar, kTile, [&](int r) -> int64_t { return (int64_t)(r0 + r) * DP; });
+      load_tr(sm.u.t.kt, kbart, kTile, [&](int d, int r) -> int64_t { return (int64_t)d * a.nblkp + r0 + r; });
+      __syncthreads();
+      dq_step<T, DP>(sm, qf, gf, dq, lse2, delta, a.scale_log2, col, grp,
+                     [&](int r) { return ((live >> r) & 1ull) != 0ull; });
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < DP / 16; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.u.st[qloc][16 * dt + 4 * grp + i] = dq[dt][i] * a.scale;
+  }
+  __syncthreads();
+  write_rows<T>(a, &sm.u.st[0][0], DP + 1, nq, b, h, qrow0, true, (T*)a.dq, sm.src, sm.rel);
+}
+
+template <typename T, int DP>
+pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
+  const dim3 tiles(d.nblk * a.tiles_per_block, d.H, d.B);
+  if (a.with_summaries) {
+    {
+      ProfileScope prof("bwd_summary", s);
+      hipLaunchKernelGGL((k_bwd_summary<T, DP>), dim3(d.nblkp / kTile, d.H, d.B * a.chunks), dim3(kThreads), 0, s, a);
+    }
+    const int64_t n = (int64_t)d.B * d.H * d.nblkp * d.Dp;
+    ProfileScope prof("bwd_reduce", s);
+    hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const float*)a.part_k, (const float*)a.part_v, a.dkbar, a.dvbar, n, a.chunks);
+  }
+  {
+    ProfileScope prof("bwd_local", s);
+    hipLaunchKernelGGL((k_bwd_local<T, DP>), tiles, dim3(kThreads), 0, s, a);
+  }
+  {
+    ProfileScope prof("bwd_dq", s);
+    hipLaunchKernelGGL((k_bwd_dq<T, DP>), tiles, dim3(kThreads), 0, s, a);
+  }
+  return check_launch("backward: attention");
+}
+
+template <typename T>
+pack3d_status launch_typed(const Dims& d, const BwdArgs& a, hipStream_t s) {
+  {
+    const int ntok = d.bvol < kTile ? d.bvol : kTile;
+    int vec = 1;
+    const int cap = 16 / (int)sizeof(T);
+    while (vec * 2 <= cap && d.half % (vec * 2) == 0) vec *= 2;
+    const size_t lds = sizeof(float) * ntok * (d.D / vec) + sizeof(T) * d.Dp * (ntok + 8);
+    const dim3 grid(d.nblk, d.H, d.B);
+    ProfileScope prof("bwd_pre", s);
+    switch (vec) {
+      case 1: hipLaunchKernelGGL((k_bwd_pre<T, 1>), grid, dim3(256), lds, s, a); break;
+      case 2: hipLaunchKernelGGL((k_bwd_pre<T, 2>), grid, dim3(256), lds, s, a); break;
+      case 4: hipLaunchKernelGGL((k_bwd_pre<T, 4>), grid, dim3(256), lds, s, a); break;
+      default:
+        if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_bwd_pre<T, 8>), grid, dim3(256), lds, s, a);
+        break;
+    }
+  }
+  pack3d_status st = check_launch("backward: preprocess");
+  if (st != PACK3D_OK) return st;
+  switch (d.Dp) {
+    case 32: return launch_dp<T, 32>(d, a, s);
+    case 64: return launch_dp<T, 64>(d, a, s);
+    case 96: return launch_dp<T, 96>(d, a, s);
+    case 128: return launch_dp<T, 128>(d, a, s);
+    default: return set_error(PACK3D_E_UNSUPPORTED, "backward: padded head dim %d", d.Dp);
+  }
+}
+
+}  // namespace
+
+pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3d_attn* at, const int32_t* coords,
+                              const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              char* ws, const Workspace& w, hipStream_t s) {
+  BwdArgs a;
+  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.qt = ws + w.qt; a.kt = ws + w.kt; a.vr = ws + w.vr;
+  a.kbar = ws + w.kbar; a.kbart = ws + w.kbart; a.vbar = ws + w.vbar;
+  a.doc = ws + w.doc; a.dot = ws + w.dot; a.lsec = (float*)(ws + w.lsec); a.delta = (float*)(ws + w.delta);
+  a.dkbar = (float*)(ws + w.dkbar); a.dvbar = (float*)(ws + w.dvbar);
+  a.part_k = (float*)(ws + w.part_k); a.part_v = (float*)(ws + w.part_v);
+  a.tab = (const float2*)(ws + w.rope);
+  a.out = out; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.coords = coords; a.perm = ix->perm; a.nbr = ix->nbr; a.geom = ix->geom;
+  a.B = d.B; a.N = d.N; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
+  a.slots = d.slots; a.radius = ix->radius;
+  a.tiles_per_block = d.bvol > kTile ? d.bvol / kTile : 1;
+  a.with_summaries = at->with_summaries ? 1 : 0;
+  a.chunks = summary_chunks(d);
+  a.half = d.half; a.emax = d.emax;
+  a.bz = ix->block[0]; a.by = ix->block[1]; a.bx = ix->block[2];
+  a.scale = at->softmax_scale > 0.f ? at->softmax_scale : 1.0f / std::sqrt((float)d.D);
+  a.scale_log2 = a.scale * kLog2e;
+  return at->dtype == PACK3D_BF16 ? launch_typed<bf16>(d, a, s) : launch_typed<float>(d, a, s);
+}
+
+}  // namespace pack3d

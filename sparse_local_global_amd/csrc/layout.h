@@ -31,29 +31,50 @@ inline Dims make_dims(const pack3d_index* ix, const pack3d_attn* at) {
   return d;
 }
 
+// Query chunks of the summary-major backward: enough workgroups to fill the chip.
+inline int summary_chunks(const Dims& d) {
+  const int base = (d.nblkp / kTile) * d.H * d.B;
+  int qc = 2048 / (base > 0 ? base : 1);
+  if (qc < 1) qc = 1;
+  if (qc > d.nblk) qc = d.nblk;
+  return qc;
+}
+
 struct Workspace {
-  // forward intermediates
+  // forward intermediates (canonical order)
   size_t rope, qrot, krot, vt, kbar, vbart, fwd_total;
   // backward extras
-  size_t doc, delta, dkbar, dvbar, bwd_total;
+  size_t qt, kt, vr, kbart, vbar, doc, dot, lsec, delta, dkbar, dvbar, part_k, part_v, bwd_total;
 };
 
 inline Workspace workspace_layout(const Dims& d) {
   Workspace w;
   const size_t bh = (size_t)d.B * d.H;
   const size_t act = bh * d.N * d.Dp * d.esize;
+  const size_t summ = bh * d.nblkp * d.Dp * d.esize;
+  const size_t summ32 = bh * d.nblkp * d.Dp * sizeof(float);
   size_t off = 0;
-  w.rope = off;  off = align_up(off + sizeof(float) * 2 * (size_t)d.emax * d.half, 256);
-  w.qrot = off;  off = align_up(off + act, 256);
-  w.krot = off;  off = align_up(off + act, 256);
-  w.vt = off;    off = align_up(off + act, 256);
-  w.kbar = off;  off = align_up(off + bh * d.nblkp * d.Dp * d.esize, 256);
-  w.vbart = off; off = align_up(off + bh * d.nblkp * d.Dp * d.esize, 256);
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  w.rope = take(sizeof(float) * 2 * (size_t)d.emax * d.half);
+  w.qrot = take(act);
+  w.krot = take(act);
+  w.vt = take(act);
+  w.kbar = take(summ);
+  w.vbart = take(summ);
   w.fwd_total = off;
-  w.doc = off;   off = align_up(off + act, 256);
-  w.delta = off; off = align_up(off + sizeof(float) * bh * d.N, 256);
-  w.dkbar = off; off = align_up(off + sizeof(float) * bh * d.nblkp * d.Dp, 256);
-  w.dvbar = off; off = align_up(off + sizeof(float) * bh * d.nblkp * d.Dp, 256);
+  w.qt = take(act);
+  w.kt = take(act);
+  w.vr = take(act);
+  w.kbart = take(summ);
+  w.vbar = take(summ);
+  w.doc = take(act);
+  w.dot = take(act);
+  w.lsec = take(sizeof(float) * bh * d.N);
+  w.delta = take(sizeof(float) * bh * d.N);
+  w.dkbar = take(summ32);
+  w.dvbar = take(summ32);
+  w.part_k = take(summ32 * summary_chunks(d));
+  w.part_v = take(summ32 * summary_chunks(d));
   w.bwd_total = off;
   return w;
 }
@@ -61,7 +82,10 @@ inline Workspace workspace_layout(const Dims& d) {
 // Launchers (defined in the kernel sources).
 pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
                                const void* q, const void* k, const void* v, const int32_t* coords,
-                               char* ws, const Workspace& w, hipStream_t s);
+                               char* ws, const Workspace& w, bool backward_layouts, hipStream_t s);
+pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3d_attn* at, const int32_t* coords,
+                              const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              char* ws, const Workspace& w, hipStream_t s);
 pack3d_status launch_attn_fwd(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
                               const char* ws, const Workspace& w, void* out, float* lse, hipStream_t s);
 

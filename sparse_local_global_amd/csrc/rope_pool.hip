@@ -51,10 +51,13 @@ struct RopeArgs {
   const int32_t* coords; const int32_t* perm; const int32_t* geom;
   const float2* tab;
   void* qrot; void* krot; void* vt; void* kbar; void* vbart;
+  // extra layouts for the backward (BWD): Q~ and K~ transposed inside each block, V
+  // row-major, block means of K~ transposed and of V row-major
+  void* qt; void* kt; void* vr; void* kbart; void* vbar;
   int N, H, D, Dp, nblk, nblkp, bvol, heads_per_group, emax, half;
 };
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool BWD>
 __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   extern __shared__ char smem[];
   const int blk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
@@ -63,13 +66,15 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   const int da = D / 3, half = a.half;
   const int ntok = bvol < kChunk ? bvol : kChunk;
   const int nchunk = bvol / ntok;
-  // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1] (float), vl[Dp][ntok+8] (T)
+  // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1] (float), vl[Dp][ntok+8] (T),
+  // and for BWD ql[ntok][Dp+1] (float)
   int* s_src = (int*)smem;
   int* s_rel = s_src + bvol;
   float* kl = (float*)(s_rel + 3 * bvol);
   const int kls = Dp + 1;
   T* vl = (T*)(kl + ntok * kls);
   const int vls = ntok + 8;
+  float* ql = (float*)(vl + Dp * vls);
 
   const int32_t* g = a.geom + b * G_FIELDS;
   for (int t = tid; t < bvol; t += 256) {
@@ -130,6 +135,10 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           ok2.v[e] = from_f<T>(ky2);
           kl[tok * kls + col1 + e] = ky1;
           kl[tok * kls + col2 + e] = ky2;
+          if constexpr (BWD) {
+            ql[tok * kls + col1 + e] = to_f(oq1.v[e]);
+            ql[tok * kls + col2 + e] = to_f(oq2.v[e]);
+          }
         }
         const int64_t out_row = (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp;
         *(Vec<T, VEC>*)(qrot + out_row + col1) = oq1;
@@ -145,6 +154,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         const Vec<T, VEC> x = *(const Vec<T, VEC>*)(v + (((int64_t)b * N + src) * H + h) * D + col);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) vl[(col + e) * vls + tok] = x.v[e];
+        if constexpr (BWD) *(Vec<T, VEC>*)((T*)a.vr + (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp + col) = x;
       }
       // zero padding columns D..Dp of qrot / krot rows and of the staged tiles
       if (Dp > D) {
@@ -156,6 +166,10 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           krot[out_row + col] = from_f<T>(0.f);
           kl[tok * kls + col] = 0.f;
           vl[col * vls + tok] = from_f<T>(0.f);
+          if constexpr (BWD) {
+            ql[tok * kls + col] = 0.f;
+            ((T*)a.vr)[out_row + col] = from_f<T>(0.f);
+          }
         }
       }
       __syncthreads();
@@ -177,6 +191,15 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           const T* srcp = vl + d * vls + c8;
 #pragma unroll
           for (int e = 0; e < 8; ++e) dst[e] = srcp[e];
+          if constexpr (BWD) {
+            // K~ and Q~ transposed inside the block, same layout as vt
+            const int64_t o = ((bh * a.nblk + blk) * Dp + d) * bvol + t0 + c8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              ((T*)a.kt)[o + e] = from_f<T>(kl[(c8 + e) * kls + d]);
+              ((T*)a.qt)[o + e] = from_f<T>(ql[(c8 + e) * kls + d]);
+            }
+          }
         }
       }
       __syncthreads();
@@ -185,40 +208,49 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
       const float inv = 1.0f / (float)bvol;
       ((T*)a.kbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(ksum * inv);
       ((T*)a.vbart)[(bh * Dp + tid) * a.nblkp + blk] = from_f<T>(vsum * inv);
+      if constexpr (BWD) {
+        ((T*)a.kbart)[(bh * Dp + tid) * a.nblkp + blk] = from_f<T>(ksum * inv);
+        ((T*)a.vbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(vsum * inv);
+      }
       // zero the padding summaries nblk .. nblkp (there may be more of them than blocks)
       for (int pad_blk = a.nblk + blk; pad_blk < a.nblkp; pad_blk += a.nblk) {
         ((T*)a.kbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
         ((T*)a.vbart)[(bh * Dp + tid) * a.nblkp + pad_blk] = from_f<T>(0.f);
+        if constexpr (BWD) {
+          ((T*)a.kbart)[(bh * Dp + tid) * a.nblkp + pad_blk] = from_f<T>(0.f);
+          ((T*)a.vbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
+        }
       }
     }
   }
 }
 
-template <typename T>
+template <typename T, bool BWD>
 pack3d_status launch_typed(const Dims& d, const RopeArgs& a, hipStream_t s) {
   const int ntok = d.bvol < kChunk ? d.bvol : kChunk;
-  const size_t lds = sizeof(int) * 4 * d.bvol + sizeof(float) * ntok * (d.Dp + 1) + sizeof(T) * d.Dp * (ntok + 8);
+  size_t lds = sizeof(int) * 4 * d.bvol + sizeof(float) * ntok * (d.Dp + 1) + sizeof(T) * d.Dp * (ntok + 8);
+  if (BWD) lds += sizeof(float) * ntok * (d.Dp + 1);
   dim3 grid(d.nblk, d.H / a.heads_per_group, d.B);
-  ProfileScope prof("rope_pool", s);
+  ProfileScope prof(BWD ? "rope_pool_bwd" : "rope_pool", s);
   int vec = 1;
   const int cap = 16 / (int)sizeof(T);
   while (vec * 2 <= cap && d.half % (vec * 2) == 0) vec *= 2;
   switch (vec) {
-    case 1: hipLaunchKernelGGL((k_rope_pool<T, 1>), grid, dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_rope_pool<T, 2>), grid, dim3(256), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_rope_pool<T, 4>), grid, dim3(256), lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_rope_pool<T, 1, BWD>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_rope_pool<T, 2, BWD>), grid, dim3(256), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_rope_pool<T, 4, BWD>), grid, dim3(256), lds, s, a); break;
     default:
-      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_rope_pool<T, 8>), grid, dim3(256), lds, s, a);
+      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_rope_pool<T, 8, BWD>), grid, dim3(256), lds, s, a);
       break;
   }
-  return check_launch("forward: rope/pool");
+  return check_launch("rope/pool");
 }
 
 }  // namespace
 
 pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
                                const void* q, const void* k, const void* v, const int32_t* coords,
-                               char* ws, const Workspace& w, hipStream_t s) {
+                               char* ws, const Workspace& w, bool backward_layouts, hipStream_t s) {
   const int n_tab = d.emax * d.half;
   {
   ProfileScope prof("rope_table", s);
@@ -229,6 +261,7 @@ pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack
   a.q = q; a.k = k; a.v = v; a.coords = coords; a.perm = ix->perm; a.geom = ix->geom;
   a.tab = (const float2*)(ws + w.rope);
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vt = ws + w.vt; a.kbar = ws + w.kbar; a.vbart = ws + w.vbart;
+  a.qt = ws + w.qt; a.kt = ws + w.kt; a.vr = ws + w.vr; a.kbart = ws + w.kbart; a.vbar = ws + w.vbar;
   a.N = d.N; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.emax = d.emax; a.half = d.half;
   // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all
@@ -237,7 +270,9 @@ pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack
     if (d.H % c == 0 && ((size_t)c * d.D * d.esize) % 128 == 0) { hp = c; break; }
   }
   a.heads_per_group = hp;
-  return at->dtype == PACK3D_BF16 ? launch_typed<bf16>(d, a, s) : launch_typed<float>(d, a, s);
+  if (backward_layouts)
+    return at->dtype == PACK3D_BF16 ? launch_typed<bf16, true>(d, a, s) : launch_typed<float, true>(d, a, s);
+  return at->dtype == PACK3D_BF16 ? launch_typed<bf16, false>(d, a, s) : launch_typed<float, false>(d, a, s);
 }
 
 }  // namespace pack3d

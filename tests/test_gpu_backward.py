@@ -1,0 +1,116 @@
+"""GPU backward (dq, dk, dv through the softmax, the block mean pooling and the RoPE)
+against the fp64 oracle.  Tolerances: max-abs 1e-5 (fp32 inputs), 2e-2 (bf16 inputs,
+fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+import sparse_local_global_amd.pack3d as p3
+from tests.gpu_cases import DEV, TOL, max_err, say, to_dev
+from tests.test_gpu_forward import CASES
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_backward(w, dtype, x=None, with_summaries=True, **kw):
+    if x is None:
+        x = si.make_inputs(w, dtype, with_grad=True, **kw)
+    xd = to_dev(x)
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    out, lse = p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], rope_base=w.rope_base,
+                          with_summaries=with_summaries)
+    dq, dk, dv = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"],
+                             rope_base=w.rope_base, with_summaries=with_summaries)
+    torch.cuda.synchronize()
+    return x, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("grid,block,r,heads,d,packing,batch,dtype", CASES)
+@pytest.mark.parametrize("with_s", [True, False])
+def test_backward_matches_oracle_small(grid, block, r, heads, d, packing, batch, dtype, with_s):
+    w = si.small_workload(grid=grid, block=block, radius=r, heads=heads, head_dim=d, packing=packing,
+                          batch=batch, seed=19)
+    say(f"backward {grid} {block} r={r} H={heads} D={d} {packing} B={batch} {dtype} summaries={with_s}")
+    x, grads = gpu_backward(w, dtype, with_summaries=with_s)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], block, r, with_summaries=with_s)
+    for name, g, rr in zip(("dq", "dk", "dv"), grads, ref):
+        err = max_err(g, rr)
+        assert err < TOL[dtype], (name, err)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_16k_workload_full(dtype):
+    w = si.WORKLOADS["16k"]
+    say(f"backward 16k {dtype}")
+    x, grads = gpu_backward(w, dtype)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius)
+    for name, g, rr in zip(("dq", "dk", "dv"), grads, ref):
+        assert max_err(g, rr) < TOL[dtype], name
+
+
+def test_backward_65k_training_workload_one_head():
+    """Full-size training step launch; the oracle computes every gradient of one (volume, head)."""
+    w = si.WORKLOADS["65k-train"]
+    dtype = torch.bfloat16
+    say("backward 65k training workload")
+    x, grads = gpu_backward(w, dtype)
+    vol, head = 1, 5
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius,
+                          volumes=[vol], heads=[head])
+    for name, g, rr in zip(("dq", "dk", "dv"), grads, ref):
+        gg = g[vol][:, head].float().cpu().double().numpy()
+        assert np.abs(gg - rr[vol][:, head]).max() < TOL[dtype], name
+        assert torch.isfinite(g).all(), name
+
+
+def test_backward_deterministic_and_repacking_bitwise():
+    w = si.small_workload(grid=(8, 8, 16), block=(4, 4, 4), heads=2, head_dim=96, packing="random", seed=6)
+    dtype = torch.bfloat16
+    _, g1 = gpu_backward(w, dtype)
+    _, g2 = gpu_backward(w, dtype)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    ref = None
+    for packing in si.PACKINGS:
+        x, g = gpu_backward(w, dtype, packing=packing)
+        inv = torch.argsort(x["perm"][0]).to(DEV)
+        g = [t[0][inv] for t in g]
+        if ref is None:
+            ref = g
+        else:
+            for a, b in zip(g, ref):
+                assert torch.equal(a, b), packing
+    _, g3 = gpu_backward(w, dtype, shift=(-9, 4, 77))
+    for a, b in zip(g1, g3):
+        assert torch.equal(a, b)
+
+
+def test_autograd_wrapper():
+    w = si.small_workload(grid=(8, 8, 8), block=(2, 2, 4), heads=2, head_dim=48, packing="morton", seed=12)
+    dtype = torch.float32
+    x = si.make_inputs(w, dtype, with_grad=True)
+    xd = to_dev(x)
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    q, k, v = (xd[n].clone().requires_grad_() for n in ("q", "k", "v"))
+    o = p3.attention(q, k, v, ix, xd["coords"])
+    (o * xd["do"]).sum().backward()
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius)
+    for g, rr in zip((q.grad, k.grad, v.grad), ref):
+        assert max_err(g, rr) < TOL[dtype]
+
+
+def test_backward_poisoned_workspace():
+    w = si.small_workload(grid=(8, 8, 16), block=(4, 4, 4), heads=2, head_dim=48, packing="random", seed=8)
+    dtype = torch.float32
+    x, g1 = gpu_backward(w, dtype)
+    xd = to_dev(x)
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    out, lse = p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"])
+    attn = p3.make_attn(dtype, w.heads, w.head_dim)
+    ws = torch.full((p3.workspace_bytes(ix, attn, True) // 4,), float("nan"), device=DEV).view(torch.uint8)
+    g2 = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
