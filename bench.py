@@ -84,6 +84,8 @@ def main(argv=None) -> int:
     ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
     ap.add_argument("--cpu-sample-blocks", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -93,6 +95,15 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return 0
     import synthetic_inputs as si
     import sparse_local_global_amd.pack3d as p3
 
@@ -157,16 +168,36 @@ def main(argv=None) -> int:
     local, summ = pair_counts(ix.tables())
     bh = w.batch * w.heads
     d = w.head_dim
-    fwd_flop = 4.0 * d * (local + summ) * bh
-    win_flop = 4.0 * d * local * bh
-    kern = {k: {"launches": n, "avg_ms": t / max(n, 1)} for k, (n, t) in prof.items()}
+    act = float(w.batch * w.tokens * w.heads * d * 2)          # one bf16 activation tensor
+    # algorithmic work per launch: (flop or bytes, bound)
+    work = {
+        "attn_fwd": (4.0 * d * (local + summ) * bh, "mfma"),
+        "attn_fwd_windowed": (4.0 * d * local * bh, "mfma"),
+        "bwd_summary": (8.0 * d * summ * bh, "mfma"),      # S, dP, dVbar, dKbar per summary pair
+        "bwd_local": (8.0 * d * local * bh, "mfma"),       # S, dP, dV, dK per local pair
+        "bwd_dq": (2.0 * d * (local + summ) * bh, "mfma"), # dQ only: S and dP are recomputed
+        "rope_pool": (6.0 * act, "hbm"),                    # read q, k, v; write Q~, K~, V^T
+        "rope_pool_bwd": (9.0 * act, "hbm"),                # plus Q~^T, K~^T, V row-major
+        "bwd_pre": (4.0 * act, "hbm"),                      # read dO, O; write dO row-major, dO^T
+    }
+    kern = {}
+    for name, (n, t) in prof.items():
+        avg = t / max(n, 1)
+        entry = {"launches": n, "avg_ms": avg, "total_ms_per_step": t / args.steps}
+        if name in work:
+            amount, bound = work[name]
+            rate = amount / (avg * 1e-3)
+            if bound == "mfma":
+                entry.update(bound="mfma", flop_per_launch=amount, tflops=rate / 1e12,
+                             frac=rate / 1e12 / PEAK_BF16_TFLOPS)
+            else:
+                entry.update(bound="hbm", bytes_per_launch=amount, gbs=rate / 1e9, frac=rate / 1e9 / PEAK_HBM_GBS)
+        kern[name] = entry
+    dominant = max((k for k in kern if kern[k].get("bound") == "mfma"), key=lambda k: kern[k]["total_ms_per_step"])
+    dk = kern[dominant]
     attn_ms = kern["attn_fwd"]["avg_ms"]
     win_attn_ms = prof_win["attn_fwd_windowed"][1] / max(prof_win["attn_fwd_windowed"][0], 1)
-    achieved = fwd_flop / (attn_ms * 1e-3) / 1e12
-    # rope/pool: reads q, k, v; writes rotated q, k and transposed v (block means are negligible)
-    elem = 2
-    rope_bytes = 6.0 * w.batch * w.tokens * w.heads * d * elem
-    rope_ms = kern["rope_pool"]["avg_ms"]
+    fwd_flop = work["attn_fwd"][0]
 
     tokens = w.batch * w.tokens
     result = {
@@ -186,18 +217,18 @@ def main(argv=None) -> int:
                    "batch": w.batch, "grid_zyx": list(w.grid), "tokens_per_volume": w.tokens,
                    "tokens_per_step": tokens, "heads": w.heads, "head_dim": d, "block_zyx": list(w.block),
                    "local_radius": w.radius, "packing": w.packing, "accumulation": "fp32"},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "flop_per_launch": fwd_flop, "avg_launch_ms": attn_ms},
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": dk["frac"], "traffic": None,
+                     "flop_per_launch": dk["flop_per_launch"], "avg_launch_ms": dk["avg_ms"]},
         "kernels": kern,
         "forward_ms": ms_fwd,
+        "forward_tokens_per_s": tokens / (ms_fwd * 1e-3),
+        "attn_fwd_tflops": fwd_flop / (attn_ms * 1e-3) / 1e12,
+        "attn_fwd_mfma_frac": fwd_flop / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "windowed_forward_ms": ms_win,
         "forward_vs_windowed": ms_fwd / ms_win,
         "attn_vs_windowed_attn": attn_ms / win_attn_ms,
-        "windowed_attn": {"avg_ms": win_attn_ms, "tflops": win_flop / (win_attn_ms * 1e-3) / 1e12},
-        "rope_pool": {"avg_ms": rope_ms, "algorithmic_bytes": rope_bytes,
-                      "gbs": rope_bytes / (rope_ms * 1e-3) / 1e9,
-                      "frac_hbm": rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "windowed_attn": {"avg_ms": win_attn_ms, "tflops": work["attn_fwd_windowed"][0] / (win_attn_ms * 1e-3) / 1e12},
         "index_build_ms": index_ms,
         "ms_per_step_with_kernel_events": ms_step_profiled,
         "pairs_per_volume_head": {"local": local, "summary": summ},

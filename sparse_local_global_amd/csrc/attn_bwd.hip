@@ -165,7 +165,7 @@ struct SumSmem {
 };
 
 template <typename T, int DP>
-__global__ __launch_bounds__(kThreads) void k_bwd_summary(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_summary(BwdArgs a) {
   __shared__ SumSmem<T, DP> sm;
   const int r0 = blockIdx.x * kTile, h = blockIdx.y;
   const int b = blockIdx.z / a.chunks, chunk = blockIdx.z - b * a.chunks;
@@ -187,42 +187,63 @@ __global__ __launch_bounds__(kThreads) void k_bwd_summary(BwdArgs a) {
   const int q_begin = (int)((int64_t)chunk * a.nblk / a.chunks);
   const int q_end = (int)((int64_t)(chunk + 1) * a.nblk / a.chunks);
   const int nrow = bvol < kTile ? bvol : kTile;
-  const T* qrot = (const T*)a.qrot + bh * N * DP;
-  const T* doc = (const T*)a.doc + bh * N * DP;
-  const T* qt = (const T*)a.qt + bh * a.nblk * DP * bvol;
-  const T* dot = (const T*)a.dot + bh * a.nblk * DP * bvol;
-  for (int qb = q_begin; qb < q_end; ++qb) {
+  const int tpb = a.tiles_per_block;
+  const size_t slice = (size_t)N * DP * sizeof(T);
+  const Src qrot((const T*)a.qrot + bh * N * DP, slice);
+  const Src doc((const T*)a.doc + bh * N * DP, slice);
+  const Src qt((const T*)a.qt + bh * N * DP, slice);
+  const Src dot((const T*)a.dot + bh * N * DP, slice);
+  const float c = a.scale_log2;
+  // tile t = (query block q_begin + t / tpb, sub-tile t % tpb); pipelined like the forward
+  const int total = (q_end - q_begin) * tpb;
+  RowRegs<T, DP> rq, rg;
+  TrRegs<T, DP> rqt, rgt;
+  float pl = INFINITY, pd = 0.f;
+  auto fetch = [&](int t) {
+    const int qb = q_begin + t / tpb, qs = t - (t / tpb) * tpb;
+    const int row0 = qb * bvol + qs * kTile;
+    rq.fetch(qrot, nrow, [&](int r) { return (row0 + r) * DP; });
+    rg.fetch(doc, nrow, [&](int r) { return (row0 + r) * DP; });
+    rqt.fetch(qt, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
+    rgt.fetch(dot, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
+    if (tid < kTile) {
+      pl = tid < nrow ? a.lsec[bh * N + row0 + tid] * kLog2e : INFINITY;
+      pd = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
+    }
+  };
+  if (total > 0) fetch(0);
+  for (int t = 0; t < total; ++t) {
+    const int qb = q_begin + t / tpb;
+    __syncthreads();
+    rq.store(sm.q);
+    rg.store(sm.g);
+    rqt.store(sm.qt);
+    rgt.store(sm.gt);
+    if (tid < kTile) {
+      sm.lse[tid] = pl;
+      sm.delta[tid] = pd;
+    }
+    __syncthreads();
+    if (t + 1 < total) fetch(t + 1);
     const int qz = qb / (nby * nbx), qy = (qb / nbx) % nby, qx = qb % nbx;
     const int cheb = max(max(abs(qz - sz), abs(qy - sy)), abs(qx - sx));
     const bool masked = sid >= a.nblk || cheb <= a.radius;
-    for (int qs = 0; qs < a.tiles_per_block; ++qs) {
-      const int row0 = qb * bvol + qs * kTile;
-      load_rows(sm.q, qrot, nrow, [&](int r) -> int64_t { return (int64_t)(row0 + r) * DP; });
-      load_rows(sm.g, doc, nrow, [&](int r) -> int64_t { return (int64_t)(row0 + r) * DP; });
-      load_tr(sm.qt, qt, nrow, [&](int d, int r) -> int64_t { return ((int64_t)qb * DP + d) * bvol + qs * kTile + r; });
-      load_tr(sm.gt, dot, nrow, [&](int d, int r) -> int64_t { return ((int64_t)qb * DP + d) * bvol + qs * kTile + r; });
-      if (tid < kTile) {
-        sm.lse[tid] = tid < nrow ? a.lsec[bh * N + row0 + tid] : INFINITY;
-        sm.delta[tid] = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
-      }
-      __syncthreads();
-      f32x4 s[4], dp[4];
-      score(sm.q, kf, s, col, grp);
-      score(sm.g, vf, dp, col, grp);
+    f32x4 s[4], dp[4];
+    score(sm.q, kf, s, col, grp);
+    score(sm.g, vf, dp, col, grp);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * grp + i;
-          const float p = masked ? 0.f : exp2f(s[mt][i] * a.scale_log2 - sm.lse[r] * kLog2e);
-          s[mt][i] = p;
-          dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * grp + i;
+        float p = fast_exp2(fmaf(s[mt][i], c, -sm.lse[r]));
+        if (masked) p = 0.f;
+        s[mt][i] = p;
+        dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
       }
-      accum(sm.gt, s, dv, col, grp);
-      accum(sm.qt, dp, dk, col, grp);
-      __syncthreads();
     }
+    accum(sm.gt, s, dv, col, grp);
+    accum(sm.qt, dp, dk, col, grp);
   }
   const int64_t base = (((int64_t)chunk * a.B * a.H + bh) * a.nblkp + sid) * DP;
 #pragma unroll
@@ -264,7 +285,7 @@ struct LocSmem {
 };
 
 template <typename T, int DP>
-__global__ __launch_bounds__(kThreads) void k_bwd_local(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_local(BwdArgs a) {
   __shared__ LocSmem<T, DP> sm;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int kb = tile / a.tiles_per_block, ks = tile - kb * a.tiles_per_block;
@@ -285,40 +306,48 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DP / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const T* qrot = (const T*)a.qrot + bh * N * DP;
-  const T* doc = (const T*)a.doc + bh * N * DP;
-  const T* qt = (const T*)a.qt + bh * a.nblk * DP * bvol;
-  const T* dot = (const T*)a.dot + bh * a.nblk * DP * bvol;
+  const size_t slice = (size_t)N * DP * sizeof(T);
+  const Src qrot((const T*)a.qrot + bh * N * DP, slice);
+  const Src doc((const T*)a.doc + bh * N * DP, slice);
+  const Src qt((const T*)a.qt + bh * N * DP, slice);
+  const Src dot((const T*)a.dot + bh * N * DP, slice);
+  const float c = a.scale_log2;
   const int nq = nloc * bvol;
   const int ntiles = (nq + kTile - 1) / kTile;
-  for (int t = 0; t < ntiles; ++t) {
+  RowRegs<T, DP> rq, rg;
+  TrRegs<T, DP> rqt, rgt;
+  float pl = INFINITY, pd = 0.f;
+  auto fetch = [&](int t) {
     const int j0 = t * kTile;
     const int valid = nq - j0 < kTile ? nq - j0 : kTile;
-    auto rowoff = [&](int r) -> int64_t {
-      const int j = j0 + r, blk = sm.list[j / bvol];
-      return ((int64_t)blk * bvol + (j - (j / bvol) * bvol)) * DP;
-    };
-    auto troff = [&](int d, int r) -> int64_t {
-      const int j = j0 + r, blk = sm.list[j / bvol];
-      return ((int64_t)blk * DP + d) * bvol + (j - (j / bvol) * bvol);
-    };
-    load_rows(sm.u.t.q, qrot, valid, rowoff);
-    load_rows(sm.u.t.g, doc, valid, rowoff);
-    load_tr(sm.u.t.qt, qt, valid, troff);
-    load_tr(sm.u.t.gt, dot, valid, troff);
+    const VirtualRows vr(sm.list, bvol, j0);
+    rq.fetch(qrot, valid, [&](int r) { return vr.row(r) * DP; });
+    rg.fetch(doc, valid, [&](int r) { return vr.row(r) * DP; });
+    rqt.fetch(qt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+    rgt.fetch(dot, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
     if (tid < kTile) {
-      const int j = j0 + tid;
-      float l = INFINITY, dl = 0.f;
+      pl = INFINITY;
+      pd = 0.f;
       if (tid < valid) {
-        const int blk = sm.list[j / bvol];
-        const int64_t row = (int64_t)blk * bvol + (j - (j / bvol) * bvol);
-        l = a.lsec[bh * N + row];
-        dl = a.delta[bh * N + row];
+        const int row = vr.row(tid);
+        pl = a.lsec[bh * N + row] * kLog2e;
+        pd = a.delta[bh * N + row];
       }
-      sm.lse[tid] = l;
-      sm.delta[tid] = dl;
+    }
+  };
+  fetch(0);
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    rq.store(sm.u.t.q);
+    rg.store(sm.u.t.g);
+    rqt.store(sm.u.t.qt);
+    rgt.store(sm.u.t.gt);
+    if (tid < kTile) {
+      sm.lse[tid] = pl;
+      sm.delta[tid] = pd;
     }
     __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
     f32x4 s[4], dp[4];
     score(sm.u.t.q, kf, s, col, grp);
     score(sm.u.t.g, vf, dp, col, grp);
@@ -327,15 +356,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * grp + i;
-        const float p = exp2f(s[mt][i] * a.scale_log2 - sm.lse[r] * kLog2e);   // lse = +inf -> 0
+        const float p = fast_exp2(fmaf(s[mt][i], c, -sm.lse[r]));   // lse = +inf -> 0
         s[mt][i] = p;
         dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
       }
     }
     accum(sm.u.t.gt, s, dv, col, grp);
     accum(sm.u.t.qt, dp, dk, col, grp);
-    __syncthreads();
   }
+  __syncthreads();  // the staging area below overlays the tiles
 
   // epilogue: dK~ = scale * acc + dKbar / |b|, dV = acc + dVbar / |b|; then R^T and scatter
   const float inv = 1.0f / (float)bvol;
@@ -378,18 +407,29 @@ struct DqSmem {
   int src[kTile], rel[kTile * 3];
 };
 
-template <typename T, int DP, typename Valid>
+// Bit r of `live` says whether tile row r is a real, unmasked key.
+template <typename T, int DP>
 __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf, const ColFrag<T, DP>& gf,
-                               f32x4 (&dq)[DP / 16], float lse2, float delta, float scale_log2, int col, int grp,
-                               Valid valid) {
+                               f32x4 (&dq)[DP / 16], float lse2, float delta, float c, int col, int grp,
+                               uint64_t live) {
   f32x4 s[4], dp[4];
   score(sm.u.t.k, qf, s, col, grp);
   score(sm.u.t.v, gf, dp, col, grp);
+  if (live != ~0ull) {
+    const uint64_t bits = live >> (4 * grp);  // row 16mt + 4grp + i -> bit 16mt + i
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint32_t w = (uint32_t)(bits >> (16 * mt));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!((w >> i) & 1u)) s[mt][i] = -INFINITY;
+    }
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = valid(16 * mt + 4 * grp + i) ? exp2f(s[mt][i] * scale_log2 - lse2) : 0.f;
+      const float p = fast_exp2(fmaf(s[mt][i], c, -lse2));
       dp[mt][i] = p * (dp[mt][i] - delta);
     }
   }
@@ -397,7 +437,7 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
 }
 
 template <typename T, int DP>
-__global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(BwdArgs a) {
   __shared__ DqSmem<T, DP> sm;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int qb = tile / a.tiles_per_block, qs = tile - qb * a.tiles_per_block;
@@ -425,48 +465,55 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DP / 16; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const T* krot = (const T*)a.krot + bh * N * DP;
-  const T* vr = (const T*)a.vr + bh * N * DP;
-  const T* kt = (const T*)a.kt + bh * a.nblk * DP * bvol;
+  const size_t slice = (size_t)N * DP * sizeof(T), sslice = (size_t)a.nblkp * DP * sizeof(T);
+  const Src krot((const T*)a.krot + bh * N * DP, slice);
+  const Src vrow((const T*)a.vr + bh * N * DP, slice);
+  const Src kt((const T*)a.kt + bh * N * DP, slice);
+  const Src kbar((const T*)a.kbar + bh * a.nblkp * DP, sslice);
+  const Src vbar((const T*)a.vbar + bh * a.nblkp * DP, sslice);
+  const Src kbart((const T*)a.kbart + bh * DP * a.nblkp, sslice);
+  const float c = a.scale_log2;
   const int nkeys = nloc * bvol;
-  const int ntiles = (nkeys + kTile - 1) / kTile;
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kTile;
-    const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
-    auto rowoff = [&](int r) -> int64_t {
-      const int j = j0 + r, blk = sm.list[j / bvol];
-      return ((int64_t)blk * bvol + (j - (j / bvol) * bvol)) * DP;
-    };
-    load_rows(sm.u.t.k, krot, valid, rowoff);
-    load_rows(sm.u.t.v, vr, valid, rowoff);
-    load_tr(sm.u.t.kt, kt, valid, [&](int d, int r) -> int64_t {
-      const int j = j0 + r, blk = sm.list[j / bvol];
-      return ((int64_t)blk * DP + d) * bvol + (j - (j / bvol) * bvol);
-    });
-    __syncthreads();
-    dq_step<T, DP>(sm, qf, gf, dq, lse2, delta, a.scale_log2, col, grp, [&](int r) { return r < valid; });
-    __syncthreads();
-  }
-  if (a.with_summaries) {
-    const T* kbar = (const T*)a.kbar + bh * a.nblkp * DP;
-    const T* vbar = (const T*)a.vbar + bh * a.nblkp * DP;
-    const T* kbart = (const T*)a.kbart + bh * DP * a.nblkp;
-    const int nst = a.nblkp / kTile;
-    for (int t = 0; t < nst; ++t) {
-      const int r0 = t * kTile;
-      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
-      const uint64_t used = ((uint64_t)sm.mask[2 * t + 1] << 32) | sm.mask[2 * t];
-      const uint64_t live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
-      if (live == 0ull) continue;
-      load_rows(sm.u.t.k, kbar, kTile, [&](int r) -> int64_t { return (int64_t)(r0 + r) * DP; });
-      load_rows(sm.u.t.v, vbar, kTile, [&](int r) -> int64_t { return (int64_t)(r0 + r) * DP; });
-      load_tr(sm.u.t.kt, kbart, kTile, [&](int d, int r) -> int64_t { return (int64_t)d * a.nblkp + r0 + r; });
-      __syncthreads();
-      dq_step<T, DP>(sm, qf, gf, dq, lse2, delta, a.scale_log2, col, grp,
-                     [&](int r) { return ((live >> r) & 1ull) != 0ull; });
-      __syncthreads();
+  const int nlt = (nkeys + kTile - 1) / kTile;
+  const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
+  RowRegs<T, DP> rk, rv;
+  TrRegs<T, DP> rkt;
+  auto fetch = [&](int t) {
+    if (t < nlt) {
+      const int j0 = t * kTile;
+      const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
+      const VirtualRows vr(sm.list, bvol, j0);
+      rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
+      rv.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
+      rkt.fetch(kt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+    } else {
+      const int r0 = (t - nlt) * kTile;
+      rk.fetch(kbar, kTile, [&](int r) { return (r0 + r) * DP; });
+      rv.fetch(vbar, kTile, [&](int r) { return (r0 + r) * DP; });
+      rkt.fetch(kbart, kTile, [&](int d, int r) { return d * a.nblkp + r0 + r; });
     }
+  };
+  fetch(0);
+  for (int t = 0; t < total; ++t) {
+    __syncthreads();
+    rk.store(sm.u.t.k);
+    rv.store(sm.u.t.v);
+    rkt.store(sm.u.t.kt);
+    __syncthreads();
+    if (t + 1 < total) fetch(t + 1);
+    uint64_t live;
+    if (t < nlt) {
+      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
+      live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+    } else {
+      const int ts = t - nlt, r0 = ts * kTile;
+      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
+      const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
+      live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
+    }
+    dq_step(sm, qf, gf, dq, lse2, delta, c, col, grp, live);
   }
+  __syncthreads();  // the staging area below overlays the tiles
 #pragma unroll
   for (int dt = 0; dt < DP / 16; ++dt) {
 #pragma unroll

@@ -47,55 +47,69 @@ struct FwdSmem {
   int nloc;
 };
 
-// Online-softmax state of one lane: query column (lane & 15).
+// Online-softmax state of one lane: query column (lane & 15).  m is the running
+// reference maximum in log2 units of the scaled logits.
 template <int DP>
 struct State {
   f32x4 o[DP / 16];
   float m, l;
 };
 
-// Scale, mask, online-softmax update and P.V for one staged tile.
-// valid(r) says whether tile row r (0..63) is a real, unmasked key.
-template <typename T, int DP, typename Valid>
-__device__ inline void tile_step(const FwdSmem<T, DP>& sm, const ColFrag<T, DP>& f, State<DP>& st, float scale_log2,
-                                 int col, int grp, Valid valid) {
+// Rescaling is lazy: the reference maximum moves only when a tile's maximum exceeds it
+// by more than kRescale (log2 units), so probabilities stay below 2^kRescale and most
+// tiles skip the accumulator rescale.  The result is exact up to rounding for any
+// reference, since numerator and denominator share it.
+constexpr float kRescale = 8.0f;
+
+// One staged tile: scores, mask, online-softmax update and P.V.  Bit r of `live` says
+// whether tile row r is a real, unmasked key; all-ones tiles skip the masking.
+template <typename T, int DP>
+__device__ inline void tile_step(const FwdSmem<T, DP>& sm, const ColFrag<T, DP>& f, State<DP>& st, float c,
+                                 int col, int grp, uint64_t live) {
   f32x4 s[4];
   score(sm.k, f, s, col, grp);
-  float mx = -INFINITY;
+  if (live != ~0ull) {
+    const uint64_t bits = live >> (4 * grp);  // row 16mt + 4grp + i -> bit 16mt + i
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint32_t w = (uint32_t)(bits >> (16 * mt));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = s[mt][i] * scale_log2;
-      if (!valid(16 * mt + 4 * grp + i)) x = -INFINITY;
-      s[mt][i] = x;
-      mx = fmaxf(mx, x);
+      for (int i = 0; i < 4; ++i)
+        if (!((w >> i) & 1u)) s[mt][i] = -INFINITY;
     }
   }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  // m_new is finite: every query's first tile holds keys of its own block
-  const float alpha = exp2f(st.m - m_new);
-  st.m = m_new;
+  mx *= c;  // scale > 0: the maximum of the scaled logits
+  if (mx > st.m + kRescale) {
+    // every query's first tile holds keys of its own block, so mx is finite here
+    const float alpha = fast_exp2(st.m - mx);
+    st.m = mx;
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DP / 16; ++dt) st.o[dt] *= alpha;
+  }
+  const float mneg = -st.m;
   float ls = 0.f;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(s[mt][i] - m_new);
+      const float p = fast_exp2(fmaf(s[mt][i], c, mneg));
       s[mt][i] = p;
       ls += p;
     }
   }
-  st.l = st.l * alpha + ls;
-#pragma unroll
-  for (int dt = 0; dt < DP / 16; ++dt) st.o[dt] *= alpha;
+  st.l += ls;
   accum(sm.vt, s, st.o, col, grp);
 }
 
 template <typename T, int DP>
-__global__ __launch_bounds__(kThreads) void k_attn_fwd(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(FwdArgs a) {
   __shared__ FwdSmem<T, DP> sm;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int qb = tile / a.tiles_per_block, qsub = tile - qb * a.tiles_per_block;
@@ -122,46 +136,52 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(FwdArgs a) {
   for (int dt = 0; dt < DP / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
+  const float c = a.scale_log2;
 
-  // local stream: the neighbour blocks' keys as one virtual list of nloc * bvol rows
-  const T* krot = (const T*)a.krot + bh * N * DP;
-  const T* vt = (const T*)a.vt + bh * a.nblk * DP * bvol;
+  // Tile sequence: the local stream (the neighbour blocks' keys as one virtual list of
+  // nloc * bvol rows) then the summary stream (all block means, local ones masked).
+  // Software pipeline: the global loads of tile t+1 are issued before tile t is computed.
+  const size_t es = sizeof(T);
+  const Src krot((const T*)a.krot + bh * N * DP, (size_t)N * DP * es);
+  const Src vt((const T*)a.vt + bh * a.nblk * DP * bvol, (size_t)N * DP * es);
+  const Src kbar((const T*)a.kbar + bh * a.nblkp * DP, (size_t)a.nblkp * DP * es);
+  const Src vbart((const T*)a.vbart + bh * DP * a.nblkp, (size_t)a.nblkp * DP * es);
   const int nkeys = nloc * bvol;
-  const int ntiles = (nkeys + kTile - 1) / kTile;
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kTile;
-    const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
-    load_rows(sm.k, krot, valid, [&](int r) -> int64_t {
-      const int j = j0 + r, blk = sm.list[j / bvol];
-      return ((int64_t)blk * bvol + (j - (j / bvol) * bvol)) * DP;
-    });
-    load_tr(sm.vt, vt, valid, [&](int d, int r) -> int64_t {
-      const int j = j0 + r, blk = sm.list[j / bvol];
-      return ((int64_t)blk * DP + d) * bvol + (j - (j / bvol) * bvol);
-    });
-    __syncthreads();
-    tile_step<T, DP>(sm, f, st, a.scale_log2, col, grp, [&](int r) { return r < valid; });
-    __syncthreads();
-  }
-
-  // summary stream
-  __syncthreads();  // the local-block bitmask is complete
-  if (a.with_summaries) {
-    const T* kbar = (const T*)a.kbar + bh * a.nblkp * DP;
-    const T* vbart = (const T*)a.vbart + bh * DP * a.nblkp;
-    const int nst = a.nblkp / kTile;
-    for (int t = 0; t < nst; ++t) {
-      const int r0 = t * kTile;
-      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
-      const uint64_t used = ((uint64_t)sm.mask[2 * t + 1] << 32) | sm.mask[2 * t];
-      const uint64_t live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
-      if (live == 0ull) continue;  // uniform: every row of this tile is local or padding
-      load_rows(sm.k, kbar, kTile, [&](int r) -> int64_t { return (int64_t)(r0 + r) * DP; });
-      load_tr(sm.vt, vbart, kTile, [&](int d, int r) -> int64_t { return (int64_t)d * a.nblkp + r0 + r; });
-      __syncthreads();
-      tile_step<T, DP>(sm, f, st, a.scale_log2, col, grp, [&](int r) { return ((live >> r) & 1ull) != 0ull; });
-      __syncthreads();
+  const int nlt = (nkeys + kTile - 1) / kTile;
+  const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
+  RowRegs<T, DP> rk;
+  TrRegs<T, DP> rv;
+  auto fetch = [&](int t) {
+    if (t < nlt) {
+      const int j0 = t * kTile;
+      const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
+      const VirtualRows vr(sm.list, bvol, j0);
+      rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
+      rv.fetch(vt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+    } else {
+      const int r0 = (t - nlt) * kTile;
+      rk.fetch(kbar, kTile, [&](int r) { return (r0 + r) * DP; });
+      rv.fetch(vbart, kTile, [&](int d, int r) { return d * a.nblkp + r0 + r; });
     }
+  };
+  fetch(0);
+  for (int t = 0; t < total; ++t) {
+    __syncthreads();  // LDS free (and, at t = 0, the local-block bitmask complete)
+    rk.store(sm.k);
+    rv.store(sm.vt);
+    __syncthreads();
+    if (t + 1 < total) fetch(t + 1);
+    uint64_t live;
+    if (t < nlt) {
+      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
+      live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+    } else {
+      const int ts = t - nlt, r0 = ts * kTile;
+      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
+      const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
+      live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
+    }
+    tile_step(sm, f, st, c, col, grp, live);
   }
 
   // epilogue: o = acc / l, lse = m ln2 + ln l, scattered back to packed order

@@ -24,6 +24,22 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// A global array addressed through a buffer resource (base in SGPRs, 32-bit byte
+// offsets in VGPRs); reads at or past `bytes` return zero.
+struct Src {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ inline Src(const void* base, size_t bytes) {
+    // num_records < 2^31, so the offset 0x80000000 used for padding rows is always out of range
+    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                          (int)(bytes > 0x7fffff00u ? 0x7fffff00u : bytes), 0x00020000);
+  }
+  __device__ inline uint4 load16(uint32_t byte_off) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+  }
+};
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <typename T> struct Pad;
 template <> struct Pad<bf16> { static constexpr int row = 8, tr = 8, vec = 8; };
 template <> struct Pad<float> { static constexpr int row = 4, tr = 4, vec = 4; };
@@ -38,24 +54,29 @@ template <typename T, int DP> struct ColFrag;
 
 template <int DP> struct ColFrag<bf16, DP> {
   bf16x8 b[DP / 32];
-  // row: start of this lane's column row (DP elements), or ok = false for a zero row
-  __device__ inline void load(const bf16* __restrict__ row, bool ok, int grp) {
+  // row: start of this lane's column row (DP elements), or ok = false for a zero row;
+  // every element is multiplied by `mul` (rounded back to bf16) when mul != 1
+  __device__ inline void load(const bf16* __restrict__ row, bool ok, int grp, float mul = 1.0f) {
 #pragma unroll
     for (int s = 0; s < DP / 32; ++s) {
       if (ok) b[s] = *(const bf16x8*)(row + 32 * s + 8 * grp);
       else b[s] = bf16x8{};
+      if (mul != 1.0f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[s][e] = (bf16)((float)b[s][e] * mul);
+      }
     }
   }
 };
 
 template <int DP> struct ColFrag<float, DP> {
   float b[DP / 4];
-  __device__ inline void load(const float* __restrict__ row, bool ok, int grp) {
+  __device__ inline void load(const float* __restrict__ row, bool ok, int grp, float mul = 1.0f) {
 #pragma unroll
     for (int s = 0; s < DP / 4; s += 4) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       if (ok) x = *(const f32x4*)(row + grp * (DP / 4) + s);
-      b[s] = x[0]; b[s + 1] = x[1]; b[s + 2] = x[2]; b[s + 3] = x[3];
+      b[s] = x[0] * mul; b[s + 1] = x[1] * mul; b[s + 2] = x[2] * mul; b[s + 3] = x[3] * mul;
     }
   }
 };
@@ -122,31 +143,96 @@ __device__ inline void accum(const TrTile<float, DP>& t, const f32x4 (&p)[4], f3
   }
 }
 
-// Cooperative 16-byte loads.  rowoff(r) = element offset of row r (r < valid), others zero.
-template <typename T, int DP, typename RowOff>
-__device__ inline void load_rows(RowTile<T, DP>& t, const T* __restrict__ src, int valid, RowOff rowoff) {
-  constexpr int V = Pad<T>::vec;
-  constexpr int chunks = kTile * DP / V;
-  for (int c = threadIdx.x; c < chunks; c += kThreads) {
-    const int row = c / (DP / V), cc = (c - row * (DP / V)) * V;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (row < valid) x = *(const uint4*)(src + rowoff(row) + cc);
-    *(uint4*)&t.x[row][cc] = x;
+// Register-staged tile copies, for a software pipeline: fetch() issues every 16-byte
+// global load of a tile at once (no dependency between them), store() writes them to
+// LDS later, so the loads of tile t+1 are in flight while tile t is computed.
+// rowoff(r) = element offset of row r (r < valid); other rows are zero.
+template <typename T, int DP>
+struct RowRegs {
+  static constexpr int V = Pad<T>::vec;
+  static constexpr int n = kTile * DP / V / kThreads;
+  static_assert(kTile * DP / V % kThreads == 0, "tile chunks must spread evenly");
+  uint4 r[n];
+  template <typename RowOff>
+  __device__ inline void fetch(const Src& src, int valid, RowOff rowoff) {
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int row = c / (DP / V), cc = (c - row * (DP / V)) * V;
+      // rows past `valid` read past the end of the buffer, which returns zero
+      const uint32_t off = row < valid ? (uint32_t)(rowoff(row) + cc) * (uint32_t)sizeof(T) : 0x80000000u;
+      r[i] = src.load16(off);
+    }
   }
-}
+  __device__ inline void store(RowTile<T, DP>& t) const {
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int row = c / (DP / V), cc = (c - row * (DP / V)) * V;
+      *(uint4*)&t.x[row][cc] = r[i];
+    }
+  }
+};
 
-// troff(d, r) = element offset of V consecutive rows r.. of column d (r a multiple of V, r < valid).
-template <typename T, int DP, typename TrOff>
-__device__ inline void load_tr(TrTile<T, DP>& t, const T* __restrict__ src, int valid, TrOff troff) {
-  constexpr int V = Pad<T>::vec;
-  constexpr int chunks = DP * kTile / V;
-  for (int c = threadIdx.x; c < chunks; c += kThreads) {
-    const int d = c / (kTile / V), r = (c - d * (kTile / V)) * V;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (r < valid) x = *(const uint4*)(src + troff(d, r));
-    *(uint4*)&t.x[d][r] = x;
+// troff(d, r) = element offset of V consecutive rows r.. of column d (r a multiple of V,
+// r < valid); other rows are zero.
+template <typename T, int DP>
+struct TrRegs {
+  static constexpr int V = Pad<T>::vec;
+  static constexpr int n = DP * kTile / V / kThreads;
+  static_assert(DP * kTile / V % kThreads == 0, "tile chunks must spread evenly");
+  uint4 r[n];
+  template <typename TrOff>
+  __device__ inline void fetch(const Src& src, int valid, TrOff troff) {
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
+      const uint32_t off = rr < valid ? (uint32_t)troff(d, rr) * (uint32_t)sizeof(T) : 0x80000000u;
+      r[i] = src.load16(off);
+    }
   }
-}
+  __device__ inline void store(TrTile<T, DP>& t) const {
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
+      *(uint4*)&t.x[d][rr] = r[i];
+    }
+  }
+};
+
+// Rows j0 .. j0+63 of the virtual concatenation of the blocks in `list` (bvol rows each,
+// canonical order).  When bvol is a multiple of 64 the tile lies inside one block and
+// every row offset follows from one base; otherwise each row finds its block.
+struct VirtualRows {
+  const int* list;
+  int bvol, j0;
+  bool one_block;
+  int blk0, off0;  // block and offset of tile row 0 when one_block
+  __device__ inline VirtualRows(const int* l, int bv, int j) : list(l), bvol(bv), j0(j) {
+    one_block = (bv & 63) == 0;
+    if (one_block) {
+      const int q = j / bv;
+      blk0 = l[q];
+      off0 = j - q * bv;
+    } else {
+      blk0 = off0 = 0;
+    }
+  }
+  // canonical row of tile row r
+  __device__ inline int row(int r) const {
+    if (one_block) return blk0 * bvol + off0 + r;
+    const int j = j0 + r, q = j / bvol;
+    return list[q] * bvol + (j - q * bvol);
+  }
+  // offset of (column d, tile row r) in a block-transposed array [nblk][dp][bvol]
+  __device__ inline int tr(int d, int r, int dp) const {
+    if (one_block) return (blk0 * dp + d) * bvol + off0 + r;
+    const int j = j0 + r, q = j / bvol;
+    return (list[q] * dp + d) * bvol + (j - q * bvol);
+  }
+};
 
 // Compact the neighbour-table row of block `blk` (wave 0 only); returns the count in *n.
 __device__ inline void compact_neighbours(const int32_t* __restrict__ nbr_row, int slots, int* list, int* n) {
