@@ -181,3 +181,12 @@ def test_query_block_sampling_matches_full():
     assert ok.sum() == 2 * 3 * 8 * 2 * 12
     assert np.array_equal(os_[ok], o[ok])
     assert np.array_equal(ls[~np.isnan(ls)], lse[~np.isnan(ls)])
+
+
+def test_dense_attention_matches_library():
+    """oracle.dense_attention (plain softmax attention with 3D RoPE) against torch SDPA on fp64 CPU."""
+    w = si.small_workload(grid=(4, 4, 6), block=(2, 2, 2), head_dim=12, heads=2, seed=27, batch=2)
+    q, k, v, c = _inputs(w)
+    od, ld = _sdpa_reference(q, k, v, c, w.rope_base)
+    o, lse = oracle.dense_attention(q, k, v, c, rope_base=w.rope_base)
+    assert np.abs(o - od).max() < 1e-12 and np.abs(lse - ld).max() < 1e-12
