@@ -164,7 +164,7 @@ struct SumSmem {
   float lse[kTile], delta[kTile];
 };
 
-template <typename T, int DP>
+template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_summary(BwdArgs a) {
   __shared__ SumSmem<T, DP> sm;
   const int r0 = blockIdx.x * kTile, h = blockIdx.y;
@@ -202,10 +202,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto fetch = [&](int t) {
     const int qb = q_begin + t / tpb, qs = t - (t / tpb) * tpb;
     const int row0 = qb * bvol + qs * kTile;
-    rq.fetch(qrot, nrow, [&](int r) { return (row0 + r) * DP; });
-    rg.fetch(doc, nrow, [&](int r) { return (row0 + r) * DP; });
-    rqt.fetch(qt, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
-    rgt.fetch(dot, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
+    if constexpr (ONE_BLOCK) {
+      rq.fetch_at(qrot, (uint32_t)row0 * DP);
+      rg.fetch_at(doc, (uint32_t)row0 * DP);
+      rqt.fetch_at(qt, (uint32_t)qb * DP * bvol + qs * kTile, bvol);
+      rgt.fetch_at(dot, (uint32_t)qb * DP * bvol + qs * kTile, bvol);
+    } else {
+      rq.fetch(qrot, nrow, [&](int r) { return (row0 + r) * DP; });
+      rg.fetch(doc, nrow, [&](int r) { return (row0 + r) * DP; });
+      rqt.fetch(qt, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
+      rgt.fetch(dot, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
+    }
     if (tid < kTile) {
       pl = tid < nrow ? a.lsec[bh * N + row0 + tid] * kLog2e : INFINITY;
       pd = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
@@ -284,7 +291,7 @@ struct LocSmem {
   int src[kTile], rel[kTile * 3];
 };
 
-template <typename T, int DP>
+template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_local(BwdArgs a) {
   __shared__ LocSmem<T, DP> sm;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -321,10 +328,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int j0 = t * kTile;
     const int valid = nq - j0 < kTile ? nq - j0 : kTile;
     const VirtualRows vr(sm.list, bvol, j0);
-    rq.fetch(qrot, valid, [&](int r) { return vr.row(r) * DP; });
-    rg.fetch(doc, valid, [&](int r) { return vr.row(r) * DP; });
-    rqt.fetch(qt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
-    rgt.fetch(dot, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+    if constexpr (ONE_BLOCK) {
+      const int row0 = vr.blk0 * bvol + vr.off0;
+      rq.fetch_at(qrot, (uint32_t)row0 * DP);
+      rg.fetch_at(doc, (uint32_t)row0 * DP);
+      rqt.fetch_at(qt, (uint32_t)vr.blk0 * DP * bvol + vr.off0, bvol);
+      rgt.fetch_at(dot, (uint32_t)vr.blk0 * DP * bvol + vr.off0, bvol);
+    } else {
+      rq.fetch(qrot, valid, [&](int r) { return vr.row(r) * DP; });
+      rg.fetch(doc, valid, [&](int r) { return vr.row(r) * DP; });
+      rqt.fetch(qt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+      rgt.fetch(dot, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+    }
     if (tid < kTile) {
       pl = INFINITY;
       pd = 0.f;
@@ -436,7 +451,7 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
   accum(sm.u.t.kt, dp, dq, col, grp);
 }
 
-template <typename T, int DP>
+template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(BwdArgs a) {
   __shared__ DqSmem<T, DP> sm;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -483,14 +498,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int j0 = t * kTile;
       const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
       const VirtualRows vr(sm.list, bvol, j0);
-      rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
-      rv.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
-      rkt.fetch(kt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+      if constexpr (ONE_BLOCK) {
+        const int row0 = vr.blk0 * bvol + vr.off0;
+        rk.fetch_at(krot, (uint32_t)row0 * DP);
+        rv.fetch_at(vrow, (uint32_t)row0 * DP);
+        rkt.fetch_at(kt, (uint32_t)vr.blk0 * DP * bvol + vr.off0, bvol);
+      } else {
+        rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
+        rv.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
+        rkt.fetch(kt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+      }
     } else {
       const int r0 = (t - nlt) * kTile;
-      rk.fetch(kbar, kTile, [&](int r) { return (r0 + r) * DP; });
-      rv.fetch(vbar, kTile, [&](int r) { return (r0 + r) * DP; });
-      rkt.fetch(kbart, kTile, [&](int d, int r) { return d * a.nblkp + r0 + r; });
+      rk.fetch_at(kbar, (uint32_t)r0 * DP);
+      rv.fetch_at(vbar, (uint32_t)r0 * DP);
+      rkt.fetch_at(kbart, r0, a.nblkp);
     }
   };
   fetch(0);
@@ -523,13 +545,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   write_rows<T>(a, &sm.u.st[0][0], DP + 1, nq, b, h, qrow0, true, (T*)a.dq, sm.src, sm.rel);
 }
 
-template <typename T, int DP>
+template <typename T, int DP, bool ONE_BLOCK>
 pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   const dim3 tiles(d.nblk * a.tiles_per_block, d.H, d.B);
   if (a.with_summaries) {
     {
       ProfileScope prof("bwd_summary", s);
-      hipLaunchKernelGGL((k_bwd_summary<T, DP>), dim3(d.nblkp / kTile, d.H, d.B * a.chunks), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((k_bwd_summary<T, DP, ONE_BLOCK>), dim3(d.nblkp / kTile, d.H, d.B * a.chunks),
+                         dim3(kThreads), 0, s, a);
     }
     const int64_t n = (int64_t)d.B * d.H * d.nblkp * d.Dp;
     ProfileScope prof("bwd_reduce", s);
@@ -538,13 +561,18 @@ pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   }
   {
     ProfileScope prof("bwd_local", s);
-    hipLaunchKernelGGL((k_bwd_local<T, DP>), tiles, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_local<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
   }
   {
     ProfileScope prof("bwd_dq", s);
-    hipLaunchKernelGGL((k_bwd_dq<T, DP>), tiles, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_dq<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
   }
   return check_launch("backward: attention");
+}
+
+template <typename T, int DP>
+pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
+  return d.bvol % kTile == 0 ? launch_dp<T, DP, true>(d, a, s) : launch_dp<T, DP, false>(d, a, s);
 }
 
 template <typename T>

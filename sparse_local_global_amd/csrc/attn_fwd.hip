@@ -108,7 +108,8 @@ __device__ inline void tile_step(const FwdSmem<T, DP>& sm, const ColFrag<T, DP>&
   accum(sm.vt, s, st.o, col, grp);
 }
 
-template <typename T, int DP>
+// ONE_BLOCK: |b| is a multiple of 64, so every 64-row tile lies inside one block.
+template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(FwdArgs a) {
   __shared__ FwdSmem<T, DP> sm;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -151,17 +152,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
   RowRegs<T, DP> rk;
   TrRegs<T, DP> rv;
+  const int tpk = bvol / kTile;  // tiles per block (ONE_BLOCK)
   auto fetch = [&](int t) {
     if (t < nlt) {
-      const int j0 = t * kTile;
-      const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
-      const VirtualRows vr(sm.list, bvol, j0);
-      rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
-      rv.fetch(vt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+      if constexpr (ONE_BLOCK) {
+        const int q = t / tpk, off = (t - q * tpk) * kTile;
+        const int blk = sm.list[q];
+        rk.fetch_at(krot, (uint32_t)(blk * bvol + off) * DP);
+        rv.fetch_at(vt, (uint32_t)blk * DP * bvol + off, bvol);
+      } else {
+        const int j0 = t * kTile;
+        const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
+        const VirtualRows vr(sm.list, bvol, j0);
+        rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
+        rv.fetch(vt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+      }
     } else {
       const int r0 = (t - nlt) * kTile;
-      rk.fetch(kbar, kTile, [&](int r) { return (r0 + r) * DP; });
-      rv.fetch(vbart, kTile, [&](int d, int r) { return d * a.nblkp + r0 + r; });
+      rk.fetch_at(kbar, (uint32_t)r0 * DP);
+      rv.fetch_at(vbart, r0, a.nblkp);
     }
   };
   fetch(0);
@@ -204,15 +213,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+template <typename T, int DP>
+void launch_dp(const Dims& d, const FwdArgs& a, dim3 grid, hipStream_t s) {
+  if (d.bvol % kTile == 0) hipLaunchKernelGGL((k_attn_fwd<T, DP, true>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_fwd<T, DP, false>), grid, dim3(kThreads), 0, s, a);
+}
+
 template <typename T>
 pack3d_status launch_typed(const Dims& d, const FwdArgs& a, hipStream_t s) {
   dim3 grid(d.nblk * a.tiles_per_block, d.H, d.B);
   ProfileScope prof(a.with_summaries ? "attn_fwd" : "attn_fwd_windowed", s);
   switch (d.Dp) {
-    case 32: hipLaunchKernelGGL((k_attn_fwd<T, 32>), grid, dim3(kThreads), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_attn_fwd<T, 64>), grid, dim3(kThreads), 0, s, a); break;
-    case 96: hipLaunchKernelGGL((k_attn_fwd<T, 96>), grid, dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_attn_fwd<T, 128>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: launch_dp<T, 32>(d, a, grid, s); break;
+    case 64: launch_dp<T, 64>(d, a, grid, s); break;
+    case 96: launch_dp<T, 96>(d, a, grid, s); break;
+    case 128: launch_dp<T, 128>(d, a, grid, s); break;
     default: return set_error(PACK3D_E_UNSUPPORTED, "forward: padded head dim %d", d.Dp);
   }
   return check_launch("forward: attention");

@@ -164,6 +164,15 @@ struct RowRegs {
       r[i] = src.load16(off);
     }
   }
+  // Tile whose rows are contiguous from element `base` (uniform across the workgroup).
+  __device__ inline void fetch_at(const Src& src, uint32_t base) {
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base * (uint32_t)sizeof(T)));
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      r[i] = src.load16(b + (uint32_t)c * (uint32_t)(V * sizeof(T)));  // row-major: chunk c at c * V
+    }
+  }
   __device__ inline void store(RowTile<T, DP>& t) const {
 #pragma unroll
     for (int i = 0; i < n; ++i) {
@@ -190,6 +199,17 @@ struct TrRegs {
       const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
       const uint32_t off = rr < valid ? (uint32_t)troff(d, rr) * (uint32_t)sizeof(T) : 0x80000000u;
       r[i] = src.load16(off);
+    }
+  }
+  // Tile whose column d starts at element base + d * stride (base uniform).
+  __device__ inline void fetch_at(const Src& src, uint32_t base, uint32_t stride) {
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base * (uint32_t)sizeof(T)));
+    const uint32_t sb = stride * (uint32_t)sizeof(T);
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
+      r[i] = src.load16(b + (uint32_t)d * sb + (uint32_t)(rr * sizeof(T)));
     }
   }
   __device__ inline void store(TrTile<T, DP>& t) const {
