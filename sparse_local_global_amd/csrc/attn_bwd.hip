@@ -167,8 +167,12 @@ struct SumSmem {
 template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_summary(BwdArgs a) {
   __shared__ SumSmem<T, DP> sm;
-  const int r0 = blockIdx.x * kTile, h = blockIdx.y;
-  const int b = blockIdx.z / a.chunks, chunk = blockIdx.z - b * a.chunks;
+  // 1-D grid over (summary tile, chunk, head, volume), summary tile fastest: the
+  // workgroups that share a chunk's query tiles run on the same XCD
+  const int nst = a.nblkp / kTile;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int r0 = (L % nst) * kTile, chunk = (L / nst) % a.chunks;
+  const int h = (L / nst / a.chunks) % a.H, b = L / nst / a.chunks / a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int N = a.N, bvol = a.bvol;
@@ -294,7 +298,9 @@ struct LocSmem {
 template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_local(BwdArgs a) {
   __shared__ LocSmem<T, DP> sm;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int ntile = a.nblk * a.tiles_per_block;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
   const int kb = tile / a.tiles_per_block, ks = tile - kb * a.tiles_per_block;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -454,7 +460,9 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
 template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(BwdArgs a) {
   __shared__ DqSmem<T, DP> sm;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int ntile = a.nblk * a.tiles_per_block;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
   const int qb = tile / a.tiles_per_block, qs = tile - qb * a.tiles_per_block;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -547,11 +555,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 template <typename T, int DP, bool ONE_BLOCK>
 pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
-  const dim3 tiles(d.nblk * a.tiles_per_block, d.H, d.B);
+  const dim3 tiles(d.nblk * a.tiles_per_block * d.H * d.B);
   if (a.with_summaries) {
     {
       ProfileScope prof("bwd_summary", s);
-      hipLaunchKernelGGL((k_bwd_summary<T, DP, ONE_BLOCK>), dim3(d.nblkp / kTile, d.H, d.B * a.chunks),
+      hipLaunchKernelGGL((k_bwd_summary<T, DP, ONE_BLOCK>), dim3(d.nblkp / kTile * a.chunks * d.H * d.B),
                          dim3(kThreads), 0, s, a);
     }
     const int64_t n = (int64_t)d.B * d.H * d.nblkp * d.Dp;

@@ -112,7 +112,10 @@ __device__ inline void tile_step(const FwdSmem<T, DP>& sm, const ColFrag<T, DP>&
 template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(FwdArgs a) {
   __shared__ FwdSmem<T, DP> sm;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // 1-D grid over (tile, head, volume), tile fastest, remapped so each XCD walks neighbouring tiles
+  const int ntile = a.nblk * a.tiles_per_block;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
   const int qb = tile / a.tiles_per_block, qsub = tile - qb * a.tiles_per_block;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -221,7 +224,7 @@ void launch_dp(const Dims& d, const FwdArgs& a, dim3 grid, hipStream_t s) {
 
 template <typename T>
 pack3d_status launch_typed(const Dims& d, const FwdArgs& a, hipStream_t s) {
-  dim3 grid(d.nblk * a.tiles_per_block, d.H, d.B);
+  dim3 grid(d.nblk * a.tiles_per_block * d.H * d.B);
   ProfileScope prof(a.with_summaries ? "attn_fwd" : "attn_fwd_windowed", s);
   switch (d.Dp) {
     case 32: launch_dp<T, 32>(d, a, grid, s); break;

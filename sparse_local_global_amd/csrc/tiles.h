@@ -41,7 +41,10 @@ struct Src {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T> struct Pad;
-template <> struct Pad<bf16> { static constexpr int row = 8, tr = 8, vec = 8; };
+// Row pads keep the LDS reads of both contraction shapes free of bank conflicts on 32
+// 4-byte banks: 208-byte K rows (16-byte reads, 8 lanes per cycle) and 136-byte V^T rows
+// (8-byte reads, 16 lanes per cycle).
+template <> struct Pad<bf16> { static constexpr int row = 8, tr = 4, vec = 8; };
 template <> struct Pad<float> { static constexpr int row = 4, tr = 4, vec = 4; };
 
 // 64 rows x DP, head dim contiguous.
@@ -217,7 +220,10 @@ struct TrRegs {
     for (int i = 0; i < n; ++i) {
       const int c = threadIdx.x + i * kThreads;
       const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
-      *(uint4*)&t.x[d][rr] = r[i];
+      // rows are 8-byte aligned (not 16): two 8-byte stores
+      uint2* p = (uint2*)&t.x[d][rr];
+      p[0] = make_uint2(r[i].x, r[i].y);
+      p[1] = make_uint2(r[i].z, r[i].w);
     }
   }
 };
@@ -253,6 +259,14 @@ struct VirtualRows {
     return (list[q] * dp + d) * bvol + (j - q * bvol);
   }
 };
+
+// Workgroups are dealt to the 8 XCDs round-robin by linear id.  Map linear id L to a
+// logical tile so that each XCD walks a contiguous range of logical tiles: neighbouring
+// tiles share their key / value tiles, which then stay in that XCD's L2.
+__device__ inline int xcd_remap(int L, int total) {
+  if (total % 8) return L;
+  return (L & 7) * (total >> 3) + (L >> 3);
+}
 
 // Compact the neighbour-table row of block `blk` (wave 0 only); returns the count in *n.
 __device__ inline void compact_neighbours(const int32_t* __restrict__ nbr_row, int slots, int* list, int* n) {
