@@ -110,7 +110,7 @@ __device__ inline void tile_step(const FwdSmem<T, DP>& sm, const ColFrag<T, DP>&
 
 // ONE_BLOCK: |b| is a multiple of 64, so every 64-row tile lies inside one block.
 template <typename T, int DP, bool ONE_BLOCK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_attn_fwd(FwdArgs a) {
   __shared__ FwdSmem<T, DP> sm;
   // 1-D grid over (tile, head, volume), tile fastest, remapped so each XCD walks neighbouring tiles
   const int ntile = a.nblk * a.tiles_per_block;
@@ -153,10 +153,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nkeys = nloc * bvol;
   const int nlt = (nkeys + kTile - 1) / kTile;
   const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
-  RowRegs<T, DP> rk;
-  TrRegs<T, DP> rv;
+  // two register stages: the loads of tile t+2 are issued while tile t is computed
+  RowRegs<T, DP> rk0, rk1;
+  TrRegs<T, DP> rv0, rv1;
   const int tpk = bvol / kTile;  // tiles per block (ONE_BLOCK)
-  auto fetch = [&](int t) {
+  auto fetch = [&](RowRegs<T, DP>& rk, TrRegs<T, DP>& rv, int t) {
     if (t < nlt) {
       if constexpr (ONE_BLOCK) {
         const int q = t / tpk, off = (t - q * tpk) * kTile;
@@ -176,13 +177,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       rv.fetch_at(vbart, r0, a.nblkp);
     }
   };
-  fetch(0);
-  for (int t = 0; t < total; ++t) {
-    __syncthreads();  // LDS free (and, at t = 0, the local-block bitmask complete)
-    rk.store(sm.k);
-    rv.store(sm.vt);
-    __syncthreads();
-    if (t + 1 < total) fetch(t + 1);
+  auto compute = [&](int t) {
     uint64_t live;
     if (t < nlt) {
       const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
@@ -194,6 +189,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
     tile_step(sm, f, st, c, col, grp, live);
+  };
+  fetch(rk0, rv0, 0);
+  if (total > 1) fetch(rk1, rv1, 1);
+  for (int t = 0; t < total; t += 2) {
+    __syncthreads();  // LDS free (and, at t = 0, the local-block bitmask complete)
+    rk0.store(sm.k);
+    rv0.store(sm.vt);
+    __syncthreads();
+    if (t + 2 < total) fetch(rk0, rv0, t + 2);
+    compute(t);
+    if (t + 1 < total) {
+      __syncthreads();
+      rk1.store(sm.k);
+      rv1.store(sm.vt);
+      __syncthreads();
+      if (t + 3 < total) fetch(rk1, rv1, t + 3);
+      compute(t + 1);
+    }
   }
 
   // epilogue: o = acc / l, lse = m ln2 + ln l, scattered back to packed order
