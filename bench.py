@@ -176,9 +176,9 @@ def main(argv=None) -> int:
         "bwd_summary": (8.0 * d * summ * bh, "mfma"),      # S, dP, dVbar, dKbar per summary pair
         "bwd_local": (8.0 * d * local * bh, "mfma"),       # S, dP, dV, dK per local pair
         "bwd_dq": (2.0 * d * (local + summ) * bh, "mfma"), # dQ only: S and dP are recomputed
-        "rope_pool": (6.0 * act, "hbm"),                    # read q, k, v; write Q~, K~, V^T
-        "rope_pool_bwd": (9.0 * act, "hbm"),                # plus Q~^T, K~^T, V row-major
-        "bwd_pre": (4.0 * act, "hbm"),                      # read dO, O; write dO row-major, dO^T
+        "rope_pool": (6.0 * act, "hbm"),                    # read q, k, v; write Q~, K~, V canonical
+        "rope_pool_bwd": (6.0 * act, "hbm"),                # the same recomputation in the backward
+        "bwd_pre": (3.0 * act, "hbm"),                      # read dO, O; write dO canonical
     }
     kern = {}
     for name, (n, t) in prof.items():

@@ -163,15 +163,13 @@ pack3d_status pack3d_backward(const pack3d_index* index, const pack3d_attn* attn
                               size_t workspace_bytes, void* stream);
 
 /* Where the forward leaves its intermediates inside the workspace (byte offsets),
- * for inspection by tests.  All arrays are in canonical order, elements of attn->dtype
- * except rope_table (float2 cos, sin).
- *   qrot, krot [B, H, N, Dp]            rotated Q and K, rows padded with zeros to Dp
- *   vt         [B, H, nblk, Dp, |b|]    V transposed inside each block
- *   kbar       [B, H, nblk_pad, Dp]     block means of the rotated K (zero padding rows)
- *   vbart      [B, H, Dp, nblk_pad]     block means of V, transposed (zero padding)
+ * for inspection by tests.  All arrays are in canonical order (block-major, raster
+ * inside each block), elements of attn->dtype except rope_table (float2 cos, sin).
+ *   qrot, krot, vrow [B, H, N, Dp]   rotated Q and K, and V, rows zero-padded to Dp
+ *   kbar, vbar [B, H, nblk_pad, Dp]  block means of the rotated K and of V (zero padding rows)
  * Rotation angles use coordinates relative to each volume's origin. */
 typedef struct pack3d_views {
-  size_t rope_table, qrot, krot, vt, kbar, vbart;
+  size_t rope_table, qrot, krot, vrow, kbar, vbar;
   int32_t head_dim_padded, nblk_padded, extent_table;
 } pack3d_views;
 pack3d_status pack3d_workspace_views(const pack3d_index* index, const pack3d_attn* attn,

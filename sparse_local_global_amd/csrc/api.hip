@@ -71,8 +71,8 @@ extern "C" pack3d_status pack3d_workspace_views(const pack3d_index* ix, const pa
   if (!out) return set_error(PACK3D_E_INVALID, "workspace_views: null output");
   Dims d = make_dims(ix, at);
   Workspace w = workspace_layout(d);
-  out->rope_table = w.rope; out->qrot = w.qrot; out->krot = w.krot; out->vt = w.vt;
-  out->kbar = w.kbar; out->vbart = w.vbart;
+  out->rope_table = w.rope; out->qrot = w.qrot; out->krot = w.krot; out->vrow = w.vr;
+  out->kbar = w.kbar; out->vbar = w.vbar;
   out->head_dim_padded = d.Dp; out->nblk_padded = d.nblkp; out->extent_table = d.emax;
   return PACK3D_OK;
 }
@@ -91,7 +91,7 @@ extern "C" pack3d_status pack3d_forward(const pack3d_index* ix, const pack3d_att
   if (ws_bytes < w.fwd_total)
     return set_error(PACK3D_E_WORKSPACE, "forward: workspace %zu bytes < %zu needed", ws_bytes, w.fwd_total);
   hipStream_t s = (hipStream_t)stream;
-  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, false, s);
+  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, "rope_pool", s);
   if (st != PACK3D_OK) return st;
   return launch_attn_fwd(d, ix, at, (const char*)ws, w, out, lse, s);
 }
@@ -111,8 +111,8 @@ extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_at
   if (ws_bytes < w.bwd_total)
     return set_error(PACK3D_E_WORKSPACE, "backward: workspace %zu bytes < %zu needed", ws_bytes, w.bwd_total);
   hipStream_t s = (hipStream_t)stream;
-  // recompute the rotated / pooled operands in every layout the gradient kernels read
-  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, true, s);
+  // recompute the rotated and pooled operands (the backward is stateless)
+  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, "rope_pool_bwd", s);
   if (st != PACK3D_OK) return st;
   return launch_attn_bwd(d, ix, at, coords, out, lse, dout, dq, dk, dv, (char*)ws, w, s);
 }

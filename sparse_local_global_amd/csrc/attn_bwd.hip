@@ -11,8 +11,7 @@
 //   dq = R(c)^T dQ~, dk = R(c)^T dK~  (R orthogonal; the mean broadcasts 1/|b| to each member).
 //
 // Kernels, in launch order (no atomics anywhere, so results are bitwise reproducible):
-//   bwd_pre      per block: delta, dO gathered to canonical order (row-major and transposed
-//                inside the block), lse gathered to canonical order
+//   bwd_pre      per block: delta, dO and lse gathered to canonical order
 //   bwd_summary  summary-major: each workgroup owns 64 summaries of one (volume, head) and a
 //                chunk of query blocks; masks the summaries local to each query block and
 //                accumulates partial dKbar, dVbar (fp32) per chunk
@@ -24,7 +23,8 @@
 //   bwd_dq       query-major (like the forward, recomputing P from lse): dQ~ over local and
 //                summary tiles; the epilogue applies R^T and scatters dq
 // The waves hold their 16 columns (keys, summaries or queries) in registers and stream
-// 64-row tiles through LDS; the two contraction shapes are the ones of tiles.h.
+// row-major 64-row tiles through LDS; the two contraction shapes are the ones of
+// tiles.h (the accumulate shape reads tile columns with the LDS transpose load).
 #include <cmath>
 
 #include "tiles.h"
@@ -34,9 +34,8 @@ namespace {
 
 struct BwdArgs {
   // forward intermediates and backward layouts (workspace, canonical order)
-  const void* qrot; const void* krot; const void* qt; const void* kt; const void* vr;
-  const void* kbar; const void* kbart; const void* vbar;
-  void* doc; void* dot; float* lsec; float* delta;
+  const void* qrot; const void* krot; const void* vr; const void* kbar; const void* vbar;
+  void* doc; float* lsec; float* delta;
   float* dkbar; float* dvbar; float* part_k; float* part_v;
   const float2* tab;
   // caller buffers (packed order)
@@ -64,9 +63,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
   const int N = a.N, D = a.D, Dp = a.Dp, bvol = a.bvol;
   const int ntok = bvol < kTile ? bvol : kTile;
   const int nch = D / VEC;
-  float* part = (float*)smem;                          // [ntok][nch]
-  T* dl = (T*)(part + ntok * nch);                     // [Dp][ntok + 8]
-  const int dls = ntok + 8;
+  float* part = (float*)smem;                          // [ntok][nch] partial dot products
   const int64_t bh = (int64_t)b * a.H + h;
   const T* dout = (const T*)a.dout;
   const T* out = (const T*)a.out;
@@ -81,10 +78,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
       const Vec<T, VEC> o = *(const Vec<T, VEC>*)(out + in);
       float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        acc += (float)g.v[e] * (float)o.v[e];
-        dl[(c + e) * dls + tok] = g.v[e];
-      }
+      for (int e = 0; e < VEC; ++e) acc += (float)g.v[e] * (float)o.v[e];
       part[it] = acc;   // it = tok * nch + chunk index
       *(Vec<T, VEC>*)(doc + (bh * N + kappa) * Dp + c) = g;
     }
@@ -93,7 +87,6 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
       for (int it = tid; it < ntok * pad; it += 256) {
         const int tok = it / pad, c = D + it - tok * pad;
         doc[(bh * N + blk * bvol + t0 + tok) * Dp + c] = (T)0.f;
-        dl[c * dls + tok] = (T)0.f;
       }
     }
     __syncthreads();
@@ -104,13 +97,6 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
       for (int c = 0; c < nch; ++c) s += part[tid * nch + c];
       a.delta[bh * N + kappa] = s;
       a.lsec[bh * N + kappa] = a.lse[bh * N + src];
-    }
-    const int per_row = ntok / 8;
-    for (int it = tid; it < Dp * per_row; it += 256) {
-      const int d = it / per_row, c8 = (it - d * per_row) * 8;
-      T* dst = (T*)a.dot + ((bh * a.nblk + blk) * Dp + d) * bvol + t0 + c8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = dl[d * dls + c8 + e];
     }
     __syncthreads();
   }
@@ -160,7 +146,6 @@ __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, in
 template <typename T, int DP>
 struct SumSmem {
   RowTile<T, DP> q, g;
-  TrTile<T, DP> qt, gt;
   float lse[kTile], delta[kTile];
 };
 
@@ -195,13 +180,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const size_t slice = (size_t)N * DP * sizeof(T);
   const Src qrot((const T*)a.qrot + bh * N * DP, slice);
   const Src doc((const T*)a.doc + bh * N * DP, slice);
-  const Src qt((const T*)a.qt + bh * N * DP, slice);
-  const Src dot((const T*)a.dot + bh * N * DP, slice);
   const float c = a.scale_log2;
   // tile t = (query block q_begin + t / tpb, sub-tile t % tpb); pipelined like the forward
   const int total = (q_end - q_begin) * tpb;
   RowRegs<T, DP> rq, rg;
-  TrRegs<T, DP> rqt, rgt;
   float pl = INFINITY, pd = 0.f;
   auto fetch = [&](int t) {
     const int qb = q_begin + t / tpb, qs = t - (t / tpb) * tpb;
@@ -209,13 +191,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (ONE_BLOCK) {
       rq.fetch_at(qrot, (uint32_t)row0 * DP);
       rg.fetch_at(doc, (uint32_t)row0 * DP);
-      rqt.fetch_at(qt, (uint32_t)qb * DP * bvol + qs * kTile, bvol);
-      rgt.fetch_at(dot, (uint32_t)qb * DP * bvol + qs * kTile, bvol);
     } else {
       rq.fetch(qrot, nrow, [&](int r) { return (row0 + r) * DP; });
       rg.fetch(doc, nrow, [&](int r) { return (row0 + r) * DP; });
-      rqt.fetch(qt, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
-      rgt.fetch(dot, nrow, [&](int d, int r) { return (qb * DP + d) * bvol + qs * kTile + r; });
     }
     if (tid < kTile) {
       pl = tid < nrow ? a.lsec[bh * N + row0 + tid] * kLog2e : INFINITY;
@@ -228,8 +206,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
     rq.store(sm.q);
     rg.store(sm.g);
-    rqt.store(sm.qt);
-    rgt.store(sm.gt);
     if (tid < kTile) {
       sm.lse[tid] = pl;
       sm.delta[tid] = pd;
@@ -253,8 +229,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
       }
     }
-    accum(sm.gt, s, dv, col, grp);
-    accum(sm.qt, dp, dk, col, grp);
+    accum(sm.g, s, dv, col, grp);
+    accum(sm.q, dp, dk, col, grp);
   }
   const int64_t base = (((int64_t)chunk * a.B * a.H + bh) * a.nblkp + sid) * DP;
 #pragma unroll
@@ -285,7 +261,6 @@ struct LocSmem {
   union {
     struct {
       RowTile<T, DP> q, g;
-      TrTile<T, DP> qt, gt;
     } t;
     float st[2][kTile][DP + 1];
   } u;
@@ -322,13 +297,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const size_t slice = (size_t)N * DP * sizeof(T);
   const Src qrot((const T*)a.qrot + bh * N * DP, slice);
   const Src doc((const T*)a.doc + bh * N * DP, slice);
-  const Src qt((const T*)a.qt + bh * N * DP, slice);
-  const Src dot((const T*)a.dot + bh * N * DP, slice);
   const float c = a.scale_log2;
   const int nq = nloc * bvol;
   const int ntiles = (nq + kTile - 1) / kTile;
   RowRegs<T, DP> rq, rg;
-  TrRegs<T, DP> rqt, rgt;
   float pl = INFINITY, pd = 0.f;
   auto fetch = [&](int t) {
     const int j0 = t * kTile;
@@ -338,13 +310,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int row0 = vr.blk0 * bvol + vr.off0;
       rq.fetch_at(qrot, (uint32_t)row0 * DP);
       rg.fetch_at(doc, (uint32_t)row0 * DP);
-      rqt.fetch_at(qt, (uint32_t)vr.blk0 * DP * bvol + vr.off0, bvol);
-      rgt.fetch_at(dot, (uint32_t)vr.blk0 * DP * bvol + vr.off0, bvol);
     } else {
       rq.fetch(qrot, valid, [&](int r) { return vr.row(r) * DP; });
       rg.fetch(doc, valid, [&](int r) { return vr.row(r) * DP; });
-      rqt.fetch(qt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
-      rgt.fetch(dot, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
     }
     if (tid < kTile) {
       pl = INFINITY;
@@ -361,8 +329,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
     rq.store(sm.u.t.q);
     rg.store(sm.u.t.g);
-    rqt.store(sm.u.t.qt);
-    rgt.store(sm.u.t.gt);
     if (tid < kTile) {
       sm.lse[tid] = pl;
       sm.delta[tid] = pd;
@@ -382,8 +348,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
       }
     }
-    accum(sm.u.t.gt, s, dv, col, grp);
-    accum(sm.u.t.qt, dp, dk, col, grp);
+    accum(sm.u.t.g, s, dv, col, grp);
+    accum(sm.u.t.q, dp, dk, col, grp);
   }
   __syncthreads();  // the staging area below overlays the tiles
 
@@ -418,7 +384,6 @@ struct DqSmem {
   union {
     struct {
       RowTile<T, DP> k, v;
-      TrTile<T, DP> kt;
     } t;
     float st[kTile][DP + 1];
   } u;
@@ -454,7 +419,7 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
       dp[mt][i] = p * (dp[mt][i] - delta);
     }
   }
-  accum(sm.u.t.kt, dp, dq, col, grp);
+  accum(sm.u.t.k, dp, dq, col, grp);
 }
 
 template <typename T, int DP, bool ONE_BLOCK>
@@ -491,16 +456,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const size_t slice = (size_t)N * DP * sizeof(T), sslice = (size_t)a.nblkp * DP * sizeof(T);
   const Src krot((const T*)a.krot + bh * N * DP, slice);
   const Src vrow((const T*)a.vr + bh * N * DP, slice);
-  const Src kt((const T*)a.kt + bh * N * DP, slice);
   const Src kbar((const T*)a.kbar + bh * a.nblkp * DP, sslice);
   const Src vbar((const T*)a.vbar + bh * a.nblkp * DP, sslice);
-  const Src kbart((const T*)a.kbart + bh * DP * a.nblkp, sslice);
   const float c = a.scale_log2;
   const int nkeys = nloc * bvol;
   const int nlt = (nkeys + kTile - 1) / kTile;
   const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
   RowRegs<T, DP> rk, rv;
-  TrRegs<T, DP> rkt;
   auto fetch = [&](int t) {
     if (t < nlt) {
       const int j0 = t * kTile;
@@ -510,17 +472,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int row0 = vr.blk0 * bvol + vr.off0;
         rk.fetch_at(krot, (uint32_t)row0 * DP);
         rv.fetch_at(vrow, (uint32_t)row0 * DP);
-        rkt.fetch_at(kt, (uint32_t)vr.blk0 * DP * bvol + vr.off0, bvol);
       } else {
         rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
         rv.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
-        rkt.fetch(kt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
       }
     } else {
       const int r0 = (t - nlt) * kTile;
       rk.fetch_at(kbar, (uint32_t)r0 * DP);
       rv.fetch_at(vbar, (uint32_t)r0 * DP);
-      rkt.fetch_at(kbart, r0, a.nblkp);
     }
   };
   fetch(0);
@@ -528,7 +487,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
     rk.store(sm.u.t.k);
     rv.store(sm.u.t.v);
-    rkt.store(sm.u.t.kt);
     __syncthreads();
     if (t + 1 < total) fetch(t + 1);
     uint64_t live;
@@ -590,7 +548,7 @@ pack3d_status launch_typed(const Dims& d, const BwdArgs& a, hipStream_t s) {
     int vec = 1;
     const int cap = 16 / (int)sizeof(T);
     while (vec * 2 <= cap && d.half % (vec * 2) == 0) vec *= 2;
-    const size_t lds = sizeof(float) * ntok * (d.D / vec) + sizeof(T) * d.Dp * (ntok + 8);
+    const size_t lds = sizeof(float) * ntok * (d.D / vec);
     const dim3 grid(d.nblk, d.H, d.B);
     ProfileScope prof("bwd_pre", s);
     switch (vec) {
@@ -619,9 +577,8 @@ pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3
                               const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                               char* ws, const Workspace& w, hipStream_t s) {
   BwdArgs a;
-  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.qt = ws + w.qt; a.kt = ws + w.kt; a.vr = ws + w.vr;
-  a.kbar = ws + w.kbar; a.kbart = ws + w.kbart; a.vbar = ws + w.vbar;
-  a.doc = ws + w.doc; a.dot = ws + w.dot; a.lsec = (float*)(ws + w.lsec); a.delta = (float*)(ws + w.delta);
+  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
+  a.doc = ws + w.doc; a.lsec = (float*)(ws + w.lsec); a.delta = (float*)(ws + w.delta);
   a.dkbar = (float*)(ws + w.dkbar); a.dvbar = (float*)(ws + w.dvbar);
   a.part_k = (float*)(ws + w.part_k); a.part_v = (float*)(ws + w.part_v);
   a.tab = (const float2*)(ws + w.rope);

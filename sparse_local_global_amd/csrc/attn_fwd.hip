@@ -14,14 +14,13 @@
 // the score tile comes out of the matrix core with one query per lane column; the
 // softmax statistics of a query then live in 4 lanes (l, l^16, l^32, l^48) and the
 // probabilities are already in the B-operand layout of O^T += V^T P^T, so P never
-// goes through LDS.  K tiles [64 keys][Dp] and V^T tiles [Dp][64 keys] are staged
-// in LDS; V is stored transposed inside each block by the RoPE kernel so the V^T
-// tile rows are contiguous in HBM.
+// goes through LDS.  K and V tiles [64 keys][Dp] are staged row-major in LDS; the
+// P.V contraction reads V's columns with the LDS transpose load.
 //   bf16: v_mfma_f32_16x16x32_bf16, fp32 accumulation, fp32 softmax (exp2).
 //   fp32: v_mfma_f32_16x16x4_f32 (full fp32 products).
 // Local tiles come from the compacted neighbour list (a virtual concatenation of
 // the neighbour blocks); summary tiles walk all block means in id order, masking
-// the local blocks with an LDS bitmask, and tiles with no unmasked row are skipped.
+// the local blocks (and the padding rows) with an LDS bitmask.
 // Deterministic: fixed reduction order, no atomics.
 #include <cmath>
 
@@ -31,7 +30,7 @@ namespace pack3d {
 namespace {
 
 struct FwdArgs {
-  const void* qrot; const void* krot; const void* vt; const void* kbar; const void* vbart;
+  const void* qrot; const void* krot; const void* vr; const void* kbar; const void* vbar;
   const int32_t* perm; const int32_t* nbr;
   void* out; float* lse;
   int N, H, D, nblk, nblkp, bvol, slots, tiles_per_block, with_summaries;
@@ -41,7 +40,7 @@ struct FwdArgs {
 template <typename T, int DP>
 struct FwdSmem {
   RowTile<T, DP> k;
-  TrTile<T, DP> vt;
+  RowTile<T, DP> v;
   int list[kMaxSlots];
   uint32_t mask[kMaxBlocks / 32];
   int nloc;
@@ -105,7 +104,7 @@ __device__ inline void tile_step(const FwdSmem<T, DP>& sm, const ColFrag<T, DP>&
     }
   }
   st.l += ls;
-  accum(sm.vt, s, st.o, col, grp);
+  accum(sm.v, s, st.o, col, grp);
 }
 
 // ONE_BLOCK: |b| is a multiple of 64, so every 64-row tile lies inside one block.
@@ -147,34 +146,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // Software pipeline: the global loads of tile t+1 are issued before tile t is computed.
   const size_t es = sizeof(T);
   const Src krot((const T*)a.krot + bh * N * DP, (size_t)N * DP * es);
-  const Src vt((const T*)a.vt + bh * a.nblk * DP * bvol, (size_t)N * DP * es);
+  const Src vrow((const T*)a.vr + bh * N * DP, (size_t)N * DP * es);
   const Src kbar((const T*)a.kbar + bh * a.nblkp * DP, (size_t)a.nblkp * DP * es);
-  const Src vbart((const T*)a.vbart + bh * DP * a.nblkp, (size_t)a.nblkp * DP * es);
+  const Src vbar((const T*)a.vbar + bh * a.nblkp * DP, (size_t)a.nblkp * DP * es);
   const int nkeys = nloc * bvol;
   const int nlt = (nkeys + kTile - 1) / kTile;
   const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
   // two register stages: the loads of tile t+2 are issued while tile t is computed
   RowRegs<T, DP> rk0, rk1;
-  TrRegs<T, DP> rv0, rv1;
+  RowRegs<T, DP> rv0, rv1;
   const int tpk = bvol / kTile;  // tiles per block (ONE_BLOCK)
-  auto fetch = [&](RowRegs<T, DP>& rk, TrRegs<T, DP>& rv, int t) {
+  auto fetch = [&](RowRegs<T, DP>& rk, RowRegs<T, DP>& rv, int t) {
     if (t < nlt) {
       if constexpr (ONE_BLOCK) {
         const int q = t / tpk, off = (t - q * tpk) * kTile;
         const int blk = sm.list[q];
         rk.fetch_at(krot, (uint32_t)(blk * bvol + off) * DP);
-        rv.fetch_at(vt, (uint32_t)blk * DP * bvol + off, bvol);
+        rv.fetch_at(vrow, (uint32_t)(blk * bvol + off) * DP);
       } else {
         const int j0 = t * kTile;
         const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
         const VirtualRows vr(sm.list, bvol, j0);
         rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
-        rv.fetch(vt, valid, [&](int d, int r) { return vr.tr(d, r, DP); });
+        rv.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
       }
     } else {
       const int r0 = (t - nlt) * kTile;
       rk.fetch_at(kbar, (uint32_t)r0 * DP);
-      rv.fetch_at(vbart, r0, a.nblkp);
+      rv.fetch_at(vbar, (uint32_t)r0 * DP);
     }
   };
   auto compute = [&](int t) {
@@ -195,14 +194,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   for (int t = 0; t < total; t += 2) {
     __syncthreads();  // LDS free (and, at t = 0, the local-block bitmask complete)
     rk0.store(sm.k);
-    rv0.store(sm.vt);
+    rv0.store(sm.v);
     __syncthreads();
     if (t + 2 < total) fetch(rk0, rv0, t + 2);
     compute(t);
     if (t + 1 < total) {
       __syncthreads();
       rk1.store(sm.k);
-      rv1.store(sm.vt);
+      rv1.store(sm.v);
       __syncthreads();
       if (t + 3 < total) fetch(rk1, rv1, t + 3);
       compute(t + 1);
@@ -254,7 +253,7 @@ pack3d_status launch_typed(const Dims& d, const FwdArgs& a, hipStream_t s) {
 pack3d_status launch_attn_fwd(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
                               const char* ws, const Workspace& w, void* out, float* lse, hipStream_t s) {
   FwdArgs a;
-  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vt = ws + w.vt; a.kbar = ws + w.kbar; a.vbart = ws + w.vbart;
+  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
   a.perm = ix->perm; a.nbr = ix->nbr; a.out = out; a.lse = lse;
   a.N = d.N; a.H = d.H; a.D = d.D; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol; a.slots = d.slots;
   a.tiles_per_block = d.bvol > kTile ? d.bvol / kTile : 1;

@@ -41,10 +41,10 @@ inline int summary_chunks(const Dims& d) {
 }
 
 struct Workspace {
-  // forward intermediates (canonical order)
-  size_t rope, qrot, krot, vt, kbar, vbart, fwd_total;
+  // forward intermediates (canonical order, row-major)
+  size_t rope, qrot, krot, vr, kbar, vbar, fwd_total;
   // backward extras
-  size_t qt, kt, vr, kbart, vbar, doc, dot, lsec, delta, dkbar, dvbar, part_k, part_v, bwd_total;
+  size_t doc, lsec, delta, dkbar, dvbar, part_k, part_v, bwd_total;
 };
 
 inline Workspace workspace_layout(const Dims& d) {
@@ -58,17 +58,11 @@ inline Workspace workspace_layout(const Dims& d) {
   w.rope = take(sizeof(float) * 2 * (size_t)d.emax * d.half);
   w.qrot = take(act);
   w.krot = take(act);
-  w.vt = take(act);
-  w.kbar = take(summ);
-  w.vbart = take(summ);
-  w.fwd_total = off;
-  w.qt = take(act);
-  w.kt = take(act);
   w.vr = take(act);
-  w.kbart = take(summ);
+  w.kbar = take(summ);
   w.vbar = take(summ);
+  w.fwd_total = off;
   w.doc = take(act);
-  w.dot = take(act);
   w.lsec = take(sizeof(float) * bh * d.N);
   w.delta = take(sizeof(float) * bh * d.N);
   w.dkbar = take(summ32);
@@ -82,7 +76,7 @@ inline Workspace workspace_layout(const Dims& d) {
 // Launchers (defined in the kernel sources).
 pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
                                const void* q, const void* k, const void* v, const int32_t* coords,
-                               char* ws, const Workspace& w, bool backward_layouts, hipStream_t s);
+                               char* ws, const Workspace& w, const char* name, hipStream_t s);
 pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3d_attn* at, const int32_t* coords,
                               const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                               char* ws, const Workspace& w, hipStream_t s);

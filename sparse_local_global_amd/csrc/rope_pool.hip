@@ -12,12 +12,11 @@
 // logit and keeps the fp32 angles small.
 //
 // One workgroup per (block, head group, volume).  The block's tokens are gathered
-// from packed order (perm), Q and K are rotated in fp32 and written in canonical
-// order [B, H, N, Dp]; V is written transposed inside the block [B, H, nblk, Dp, |b|]
-// (the layout the attention kernel's P.V contraction reads); the block means of the
-// rotated K (kbar [B, H, nblkp, Dp]) and of V (vbart [B, H, Dp, nblkp]) are summed in
-// a fixed order from LDS, so results are bitwise reproducible and independent of
-// the packing.  HBM bound: reads q, k, v once, writes qrot, krot, vt once.
+// from packed order (perm); Q and K are rotated in fp32 and written with V in
+// canonical order [B, H, N, Dp] (rows zero-padded to Dp); the block means of the
+// rotated K and of V ([B, H, nblkp, Dp], zero padding rows) are summed in a fixed
+// order from LDS, so results are bitwise reproducible and independent of the
+// packing.  HBM bound: reads q, k, v once, writes the rotated Q, K and V once.
 #include <cmath>
 
 #include "layout.h"
@@ -50,14 +49,11 @@ struct RopeArgs {
   const void* q; const void* k; const void* v;
   const int32_t* coords; const int32_t* perm; const int32_t* geom;
   const float2* tab;
-  void* qrot; void* krot; void* vt; void* kbar; void* vbart;
-  // extra layouts for the backward (BWD): Q~ and K~ transposed inside each block, V
-  // row-major, block means of K~ transposed and of V row-major
-  void* qt; void* kt; void* vr; void* kbart; void* vbar;
+  void* qrot; void* krot; void* vr; void* kbar; void* vbar;
   int N, H, D, Dp, nblk, nblkp, bvol, heads_per_group, emax, half;
 };
 
-template <typename T, int VEC, bool BWD>
+template <typename T, int VEC>
 __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   extern __shared__ char smem[];
   const int blk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
@@ -66,15 +62,12 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   const int da = D / 3, half = a.half;
   const int ntok = bvol < kChunk ? bvol : kChunk;
   const int nchunk = bvol / ntok;
-  // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1] (float), vl[Dp][ntok+8] (T),
-  // and for BWD ql[ntok][Dp+1] (float)
+  // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1], vl[ntok][Dp+1] (float)
   int* s_src = (int*)smem;
   int* s_rel = s_src + bvol;
   float* kl = (float*)(s_rel + 3 * bvol);
-  const int kls = Dp + 1;
-  T* vl = (T*)(kl + ntok * kls);
-  const int vls = ntok + 8;
-  float* ql = (float*)(vl + Dp * vls);
+  const int ls = Dp + 1;
+  float* vl = kl + ntok * ls;
 
   const int32_t* g = a.geom + b * G_FIELDS;
   for (int t = tid; t < bvol; t += 256) {
@@ -95,7 +88,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   const T* v = (const T*)a.v;
   T* qrot = (T*)a.qrot;
   T* krot = (T*)a.krot;
-  T* vt = (T*)a.vt;
+  T* vr = (T*)a.vr;
   const int pchunks = half / VEC;         // VEC-wide pieces per half group
   const int rope_items = ntok * 3 * pchunks;
   const int v_items = ntok * (D / VEC);
@@ -133,12 +126,8 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           const float ky2 = y1 * r.y + y2 * r.x;
           ok1.v[e] = from_f<T>(ky1);
           ok2.v[e] = from_f<T>(ky2);
-          kl[tok * kls + col1 + e] = ky1;
-          kl[tok * kls + col2 + e] = ky2;
-          if constexpr (BWD) {
-            ql[tok * kls + col1 + e] = to_f(oq1.v[e]);
-            ql[tok * kls + col2 + e] = to_f(oq2.v[e]);
-          }
+          kl[tok * ls + col1 + e] = ky1;
+          kl[tok * ls + col2 + e] = ky2;
         }
         const int64_t out_row = (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp;
         *(Vec<T, VEC>*)(qrot + out_row + col1) = oq1;
@@ -146,17 +135,17 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         *(Vec<T, VEC>*)(krot + out_row + col1) = ok1;
         *(Vec<T, VEC>*)(krot + out_row + col2) = ok2;
       }
-      // copy v into the transposed LDS tile
+      // copy v to canonical order
       for (int it = tid; it < v_items; it += 256) {
         const int tok = it / (D / VEC);
         const int col = (it - tok * (D / VEC)) * VEC;
         const int src = s_src[t0 + tok];
         const Vec<T, VEC> x = *(const Vec<T, VEC>*)(v + (((int64_t)b * N + src) * H + h) * D + col);
+        *(Vec<T, VEC>*)(vr + (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp + col) = x;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) vl[(col + e) * vls + tok] = x.v[e];
-        if constexpr (BWD) *(Vec<T, VEC>*)((T*)a.vr + (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp + col) = x;
+        for (int e = 0; e < VEC; ++e) vl[tok * ls + col + e] = to_f(x.v[e]);
       }
-      // zero padding columns D..Dp of qrot / krot rows and of the staged tiles
+      // zero padding columns D..Dp of the rows and of the staged tiles
       if (Dp > D) {
         const int pad = Dp - D;
         for (int it = tid; it < ntok * pad; it += 256) {
@@ -164,83 +153,51 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           const int64_t out_row = (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp;
           qrot[out_row + col] = from_f<T>(0.f);
           krot[out_row + col] = from_f<T>(0.f);
-          kl[tok * kls + col] = 0.f;
-          vl[col * vls + tok] = from_f<T>(0.f);
-          if constexpr (BWD) {
-            ql[tok * kls + col] = 0.f;
-            ((T*)a.vr)[out_row + col] = from_f<T>(0.f);
-          }
+          vr[out_row + col] = from_f<T>(0.f);
+          kl[tok * ls + col] = 0.f;
+          vl[tok * ls + col] = 0.f;
         }
       }
       __syncthreads();
       if (tid < Dp) {
         float ks = 0.f, vs = 0.f;
         for (int t = 0; t < ntok; ++t) {
-          ks += kl[t * kls + tid];
-          vs += to_f(vl[tid * vls + t]);
+          ks += kl[t * ls + tid];
+          vs += vl[t * ls + tid];
         }
         ksum += ks;
         vsum += vs;
-      }
-      // write V transposed inside the block: vt[bh][blk][d][t0 .. t0+ntok)
-      {
-        const int per_row = ntok / 8;
-        for (int it = tid; it < Dp * per_row; it += 256) {
-          const int d = it / per_row, c8 = (it - d * per_row) * 8;
-          T* dst = vt + ((bh * a.nblk + blk) * Dp + d) * bvol + t0 + c8;
-          const T* srcp = vl + d * vls + c8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dst[e] = srcp[e];
-          if constexpr (BWD) {
-            // K~ and Q~ transposed inside the block, same layout as vt
-            const int64_t o = ((bh * a.nblk + blk) * Dp + d) * bvol + t0 + c8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              ((T*)a.kt)[o + e] = from_f<T>(kl[(c8 + e) * kls + d]);
-              ((T*)a.qt)[o + e] = from_f<T>(ql[(c8 + e) * kls + d]);
-            }
-          }
-        }
       }
       __syncthreads();
     }
     if (tid < Dp) {
       const float inv = 1.0f / (float)bvol;
       ((T*)a.kbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(ksum * inv);
-      ((T*)a.vbart)[(bh * Dp + tid) * a.nblkp + blk] = from_f<T>(vsum * inv);
-      if constexpr (BWD) {
-        ((T*)a.kbart)[(bh * Dp + tid) * a.nblkp + blk] = from_f<T>(ksum * inv);
-        ((T*)a.vbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(vsum * inv);
-      }
+      ((T*)a.vbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(vsum * inv);
       // zero the padding summaries nblk .. nblkp (there may be more of them than blocks)
       for (int pad_blk = a.nblk + blk; pad_blk < a.nblkp; pad_blk += a.nblk) {
         ((T*)a.kbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
-        ((T*)a.vbart)[(bh * Dp + tid) * a.nblkp + pad_blk] = from_f<T>(0.f);
-        if constexpr (BWD) {
-          ((T*)a.kbart)[(bh * Dp + tid) * a.nblkp + pad_blk] = from_f<T>(0.f);
-          ((T*)a.vbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
-        }
+        ((T*)a.vbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
       }
     }
   }
 }
 
-template <typename T, bool BWD>
-pack3d_status launch_typed(const Dims& d, const RopeArgs& a, hipStream_t s) {
+template <typename T>
+pack3d_status launch_typed(const Dims& d, const RopeArgs& a, const char* name, hipStream_t s) {
   const int ntok = d.bvol < kChunk ? d.bvol : kChunk;
-  size_t lds = sizeof(int) * 4 * d.bvol + sizeof(float) * ntok * (d.Dp + 1) + sizeof(T) * d.Dp * (ntok + 8);
-  if (BWD) lds += sizeof(float) * ntok * (d.Dp + 1);
+  const size_t lds = sizeof(int) * 4 * d.bvol + 2 * sizeof(float) * ntok * (d.Dp + 1);
   dim3 grid(d.nblk, d.H / a.heads_per_group, d.B);
-  ProfileScope prof(BWD ? "rope_pool_bwd" : "rope_pool", s);
+  ProfileScope prof(name, s);
   int vec = 1;
   const int cap = 16 / (int)sizeof(T);
   while (vec * 2 <= cap && d.half % (vec * 2) == 0) vec *= 2;
   switch (vec) {
-    case 1: hipLaunchKernelGGL((k_rope_pool<T, 1, BWD>), grid, dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_rope_pool<T, 2, BWD>), grid, dim3(256), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_rope_pool<T, 4, BWD>), grid, dim3(256), lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_rope_pool<T, 1>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_rope_pool<T, 2>), grid, dim3(256), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_rope_pool<T, 4>), grid, dim3(256), lds, s, a); break;
     default:
-      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_rope_pool<T, 8, BWD>), grid, dim3(256), lds, s, a);
+      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_rope_pool<T, 8>), grid, dim3(256), lds, s, a);
       break;
   }
   return check_launch("rope/pool");
@@ -250,18 +207,17 @@ pack3d_status launch_typed(const Dims& d, const RopeArgs& a, hipStream_t s) {
 
 pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
                                const void* q, const void* k, const void* v, const int32_t* coords,
-                               char* ws, const Workspace& w, bool backward_layouts, hipStream_t s) {
+                               char* ws, const Workspace& w, const char* name, hipStream_t s) {
   const int n_tab = d.emax * d.half;
   {
-  ProfileScope prof("rope_table", s);
-  hipLaunchKernelGGL(k_rope_table, dim3((n_tab + 255) / 256), dim3(256), 0, s,
-                     (float2*)(ws + w.rope), d.emax, d.half, d.D / 3, (double)at->rope_base);
+    ProfileScope prof("rope_table", s);
+    hipLaunchKernelGGL(k_rope_table, dim3((n_tab + 255) / 256), dim3(256), 0, s,
+                       (float2*)(ws + w.rope), d.emax, d.half, d.D / 3, (double)at->rope_base);
   }
   RopeArgs a;
   a.q = q; a.k = k; a.v = v; a.coords = coords; a.perm = ix->perm; a.geom = ix->geom;
   a.tab = (const float2*)(ws + w.rope);
-  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vt = ws + w.vt; a.kbar = ws + w.kbar; a.vbart = ws + w.vbart;
-  a.qt = ws + w.qt; a.kt = ws + w.kt; a.vr = ws + w.vr; a.kbart = ws + w.kbart; a.vbar = ws + w.vbar;
+  a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
   a.N = d.N; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.emax = d.emax; a.half = d.half;
   // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all
@@ -270,9 +226,7 @@ pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack
     if (d.H % c == 0 && ((size_t)c * d.D * d.esize) % 128 == 0) { hp = c; break; }
   }
   a.heads_per_group = hp;
-  if (backward_layouts)
-    return at->dtype == PACK3D_BF16 ? launch_typed<bf16, true>(d, a, s) : launch_typed<float, true>(d, a, s);
-  return at->dtype == PACK3D_BF16 ? launch_typed<bf16, false>(d, a, s) : launch_typed<float, false>(d, a, s);
+  return at->dtype == PACK3D_BF16 ? launch_typed<bf16>(d, a, name, s) : launch_typed<float>(d, a, name, s);
 }
 
 }  // namespace pack3d

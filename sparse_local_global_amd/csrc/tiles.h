@@ -3,17 +3,20 @@
 // Every contraction of the operator has one of two shapes, for a wave that owns
 // 16 "columns" (queries in the query-major kernels, keys or summaries in the
 // key-major ones) and streams 64 "rows" through LDS:
-//   score:  s[r][c]   = sum_d  R[r][d] * C[c][d]        (R: 64 LDS rows, C: 16 register rows)
-//   accum:  acc[d][c] += sum_r RT[d][r] * p[r][c]        (RT: the 64 rows transposed in LDS,
-//                                                         p: a score tile in accumulator layout)
-// The score tile leaves the matrix core with one column per lane (lane & 15) and
-// rows 16*mt + 4*(lane >> 4) + i, which is exactly the B-operand layout the accum
-// contraction needs, so scores never travel through LDS.
-//   bf16: v_mfma_f32_16x16x32_bf16 (fp32 accumulate).  In both operands k slot e of
-//         lane group g is head dim 32s + 8g + e (score) or row 32c + 4g + e (e < 4) /
-//         32c + 16 + 4g + (e - 4) (e >= 4) (accum).
-//   fp32: v_mfma_f32_16x16x4_f32.  k index g is head dim g*DP/4 + s (score) or row
-//         16mt + 4g + i (accum, one MFMA per i).
+//   score:  s[r][c]   = sum_d  X[r][d] * C[c][d]        (X: 64 LDS rows, C: 16 register rows)
+//   accum:  acc[d][c] += sum_r X[r][d] * p[r][c]         (X: 64 LDS rows, p: a score tile
+//                                                         in accumulator layout)
+// Both read the same row-major tile X[64][DP].  The score tile leaves the matrix core
+// with one column per lane (lane & 15) and rows 16*mt + 4*(lane >> 4) + i, which is the
+// B-operand layout the accum contraction needs, so scores never travel through LDS.
+//   bf16: v_mfma_f32_16x16x32_bf16 (fp32 accumulate).  score: k slot e of lane group g
+//         is head dim 32s + 8g + e.  accum: k slot e is row 32c + 4g + e (e < 4) or
+//         32c + 16 + 4g + (e - 4) (e >= 4); its A operand (rows of column d) is read with
+//         the LDS transpose load ds_read_b64_tr_b16, which hands lane i of a 16-lane group
+//         the 4 rows r0..r0+3 of column c0 + i when lane j points at row r0 + j/4,
+//         columns c0 + 4*(j%4) .. +3.
+//   fp32: v_mfma_f32_16x16x4_f32.  score: k index g is head dim g*DP/4 + s; accum: k
+//         index g is row 16mt + 4g + i (one MFMA per i, A read as single dwords).
 #pragma once
 
 #include "layout.h"
@@ -40,58 +43,65 @@ struct Src {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T> struct Pad;
-// Row pads keep the LDS reads of both contraction shapes free of bank conflicts on 32
-// 4-byte banks: 208-byte K rows (16-byte reads, 8 lanes per cycle) and 136-byte V^T rows
-// (8-byte reads, 16 lanes per cycle).
-template <> struct Pad<bf16> { static constexpr int row = 8, tr = 4, vec = 8; };
-template <> struct Pad<float> { static constexpr int row = 4, tr = 4, vec = 4; };
+// LDS row tile X[64][DP] (head dim contiguous).
+//   bf16: rows of RS elements, RS = DP when DP/32 is odd, else DP + 32, so that the row
+//   stride is 16 banks modulo 32; the 16-byte chunk c of row r is stored at chunk
+//   c ^ swz(r), swz(r) = 2*((r>>1)&1) + ((r>>2)&1).  This keeps the 128-bit score reads
+//   (8 consecutive rows, one chunk) and the transpose reads (4 consecutive rows, two
+//   chunks) free of bank conflicts.
+//   fp32: rows of DP + 4 floats, no swizzle.
+template <typename T, int DP> struct TileGeom;
+template <int DP> struct TileGeom<bf16, DP> {
+  static constexpr int RS = ((DP / 32) & 1) ? DP : DP + 32;
+  static constexpr int vec = 8;
+  __device__ static inline int swz(int r) { return (((r >> 1) & 1) << 1) | ((r >> 2) & 1); }
+  // element offset of chunk c (8 elements) of row r
+  __device__ static inline int chunk(int r, int c) { return r * RS + ((c ^ swz(r)) << 3); }
+};
+template <int DP> struct TileGeom<float, DP> {
+  static constexpr int RS = DP + 4;
+  static constexpr int vec = 4;
+  __device__ static inline int chunk(int r, int c) { return r * RS + (c << 2); }
+};
 
-// 64 rows x DP, head dim contiguous.
-template <typename T, int DP> struct alignas(16) RowTile { T x[kTile][DP + Pad<T>::row]; };
-// DP x 64, the 64 rows contiguous.
-template <typename T, int DP> struct alignas(16) TrTile { T x[DP][kTile + Pad<T>::tr]; };
+template <typename T, int DP> struct alignas(16) RowTile { T x[kTile * TileGeom<T, DP>::RS]; };
 
 // The 16 register rows of a wave (B operand of score).
 template <typename T, int DP> struct ColFrag;
 
 template <int DP> struct ColFrag<bf16, DP> {
   bf16x8 b[DP / 32];
-  // row: start of this lane's column row (DP elements), or ok = false for a zero row;
-  // every element is multiplied by `mul` (rounded back to bf16) when mul != 1
-  __device__ inline void load(const bf16* __restrict__ row, bool ok, int grp, float mul = 1.0f) {
+  // row: start of this lane's column row (DP elements), or ok = false for a zero row
+  __device__ inline void load(const bf16* __restrict__ row, bool ok, int grp) {
 #pragma unroll
     for (int s = 0; s < DP / 32; ++s) {
       if (ok) b[s] = *(const bf16x8*)(row + 32 * s + 8 * grp);
       else b[s] = bf16x8{};
-      if (mul != 1.0f) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) b[s][e] = (bf16)((float)b[s][e] * mul);
-      }
     }
   }
 };
 
 template <int DP> struct ColFrag<float, DP> {
   float b[DP / 4];
-  __device__ inline void load(const float* __restrict__ row, bool ok, int grp, float mul = 1.0f) {
+  __device__ inline void load(const float* __restrict__ row, bool ok, int grp) {
 #pragma unroll
     for (int s = 0; s < DP / 4; s += 4) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       if (ok) x = *(const f32x4*)(row + grp * (DP / 4) + s);
-      b[s] = x[0] * mul; b[s + 1] = x[1] * mul; b[s + 2] = x[2] * mul; b[s + 3] = x[3] * mul;
+      b[s] = x[0]; b[s + 1] = x[1]; b[s + 2] = x[2]; b[s + 3] = x[3];
     }
   }
 };
 
 template <int DP>
 __device__ inline void score(const RowTile<bf16, DP>& t, const ColFrag<bf16, DP>& f, f32x4 (&s)[4], int col, int grp) {
+  using G = TileGeom<bf16, DP>;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < DP / 32; ++k) {
-      const bf16x8 a = *(const bf16x8*)&t.x[16 * mt + col][32 * k + 8 * grp];
+      const bf16x8 a = *(const bf16x8*)&t.x[G::chunk(16 * mt + col, 4 * k + grp)];
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, f.b[k], acc, 0, 0, 0);
     }
     s[mt] = acc;
@@ -100,12 +110,13 @@ __device__ inline void score(const RowTile<bf16, DP>& t, const ColFrag<bf16, DP>
 
 template <int DP>
 __device__ inline void score(const RowTile<float, DP>& t, const ColFrag<float, DP>& f, f32x4 (&s)[4], int col, int grp) {
+  using G = TileGeom<float, DP>;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < DP / 4; k += 4) {
-      const f32x4 a = *(const f32x4*)&t.x[16 * mt + col][grp * (DP / 4) + k];
+      const f32x4 a = *(const f32x4*)&t.x[(16 * mt + col) * G::RS + grp * (DP / 4) + k];
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], f.b[k + e], acc, 0, 0, 0);
     }
@@ -113,8 +124,24 @@ __device__ inline void score(const RowTile<float, DP>& t, const ColFrag<float, D
   }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+
+// Transpose read: rows r0 .. r0+3 of column c0 + (lane & 15), for this lane's 16-lane group.
 template <int DP>
-__device__ inline void accum(const TrTile<bf16, DP>& t, const f32x4 (&p)[4], f32x4 (&acc)[DP / 16], int col, int grp) {
+__device__ inline bf16x4 read_column4(const RowTile<bf16, DP>& t, int r0, int c0, int lane16) {
+  using G = TileGeom<bf16, DP>;
+  const int r = r0 + (lane16 >> 2);
+  const int c = c0 + 4 * (lane16 & 3);  // first column of this lane's 4-element piece
+  const int off = G::chunk(r, c >> 3) + (c & 7);
+  const lds_bf16* base = (const lds_bf16*)t.x;
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + off));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+template <int DP>
+__device__ inline void accum(const RowTile<bf16, DP>& t, const f32x4 (&p)[4], f32x4 (&acc)[DP / 16], int col, int grp) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     bf16x8 b;
@@ -125,8 +152,8 @@ __device__ inline void accum(const TrTile<bf16, DP>& t, const f32x4 (&p)[4], f32
     }
 #pragma unroll
     for (int dt = 0; dt < DP / 16; ++dt) {
-      const bf16x4 lo = *(const bf16x4*)&t.x[16 * dt + col][32 * c + 4 * grp];
-      const bf16x4 hi = *(const bf16x4*)&t.x[16 * dt + col][32 * c + 16 + 4 * grp];
+      const bf16x4 lo = read_column4(t, 32 * c + 4 * grp, 16 * dt, col);
+      const bf16x4 hi = read_column4(t, 32 * c + 16 + 4 * grp, 16 * dt, col);
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[dt], 0, 0, 0);
     }
@@ -134,28 +161,32 @@ __device__ inline void accum(const TrTile<bf16, DP>& t, const f32x4 (&p)[4], f32
 }
 
 template <int DP>
-__device__ inline void accum(const TrTile<float, DP>& t, const f32x4 (&p)[4], f32x4 (&acc)[DP / 16], int col, int grp) {
+__device__ inline void accum(const RowTile<float, DP>& t, const f32x4 (&p)[4], f32x4 (&acc)[DP / 16], int col, int grp) {
+  using G = TileGeom<float, DP>;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-    for (int dt = 0; dt < DP / 16; ++dt) {
-      const f32x4 a = *(const f32x4*)&t.x[16 * dt + col][16 * mt + 4 * grp];
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * grp + i;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], p[mt][i], acc[dt], 0, 0, 0);
+      for (int dt = 0; dt < DP / 16; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.x[r * G::RS + 16 * dt + col], p[mt][i], acc[dt], 0, 0, 0);
     }
   }
 }
 
 // Register-staged tile copies, for a software pipeline: fetch() issues every 16-byte
 // global load of a tile at once (no dependency between them), store() writes them to
-// LDS later, so the loads of tile t+1 are in flight while tile t is computed.
-// rowoff(r) = element offset of row r (r < valid); other rows are zero.
+// LDS later, so the loads of a later tile are in flight while the current one is
+// computed.
 template <typename T, int DP>
 struct RowRegs {
-  static constexpr int V = Pad<T>::vec;
+  using G = TileGeom<T, DP>;
+  static constexpr int V = G::vec;
   static constexpr int n = kTile * DP / V / kThreads;
   static_assert(kTile * DP / V % kThreads == 0, "tile chunks must spread evenly");
   uint4 r[n];
+  // rowoff(r) = element offset of row r (r < valid); rows past `valid` read zero
   template <typename RowOff>
   __device__ inline void fetch(const Src& src, int valid, RowOff rowoff) {
 #pragma unroll
@@ -180,50 +211,8 @@ struct RowRegs {
 #pragma unroll
     for (int i = 0; i < n; ++i) {
       const int c = threadIdx.x + i * kThreads;
-      const int row = c / (DP / V), cc = (c - row * (DP / V)) * V;
-      *(uint4*)&t.x[row][cc] = r[i];
-    }
-  }
-};
-
-// troff(d, r) = element offset of V consecutive rows r.. of column d (r a multiple of V,
-// r < valid); other rows are zero.
-template <typename T, int DP>
-struct TrRegs {
-  static constexpr int V = Pad<T>::vec;
-  static constexpr int n = DP * kTile / V / kThreads;
-  static_assert(DP * kTile / V % kThreads == 0, "tile chunks must spread evenly");
-  uint4 r[n];
-  template <typename TrOff>
-  __device__ inline void fetch(const Src& src, int valid, TrOff troff) {
-#pragma unroll
-    for (int i = 0; i < n; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
-      const uint32_t off = rr < valid ? (uint32_t)troff(d, rr) * (uint32_t)sizeof(T) : 0x80000000u;
-      r[i] = src.load16(off);
-    }
-  }
-  // Tile whose column d starts at element base + d * stride (base uniform).
-  __device__ inline void fetch_at(const Src& src, uint32_t base, uint32_t stride) {
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base * (uint32_t)sizeof(T)));
-    const uint32_t sb = stride * (uint32_t)sizeof(T);
-#pragma unroll
-    for (int i = 0; i < n; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
-      r[i] = src.load16(b + (uint32_t)d * sb + (uint32_t)(rr * sizeof(T)));
-    }
-  }
-  __device__ inline void store(TrTile<T, DP>& t) const {
-#pragma unroll
-    for (int i = 0; i < n; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int d = c / (kTile / V), rr = (c - d * (kTile / V)) * V;
-      // rows are 8-byte aligned (not 16): two 8-byte stores
-      uint2* p = (uint2*)&t.x[d][rr];
-      p[0] = make_uint2(r[i].x, r[i].y);
-      p[1] = make_uint2(r[i].z, r[i].w);
+      const int row = c / (DP / V), ch = c - row * (DP / V);
+      *(uint4*)&t.x[G::chunk(row, ch)] = r[i];
     }
   }
 };
@@ -251,12 +240,6 @@ struct VirtualRows {
     if (one_block) return blk0 * bvol + off0 + r;
     const int j = j0 + r, q = j / bvol;
     return list[q] * bvol + (j - q * bvol);
-  }
-  // offset of (column d, tile row r) in a block-transposed array [nblk][dp][bvol]
-  __device__ inline int tr(int d, int r, int dp) const {
-    if (one_block) return (blk0 * dp + d) * bvol + off0 + r;
-    const int j = j0 + r, q = j / bvol;
-    return (list[q] * dp + d) * bvol + (j - q * bvol);
   }
 };
 

@@ -47,7 +47,7 @@ class Tables(ctypes.Structure):
 
 class Views(ctypes.Structure):
     _fields_ = [("rope_table", ctypes.c_size_t), ("qrot", ctypes.c_size_t), ("krot", ctypes.c_size_t),
-                ("vt", ctypes.c_size_t), ("kbar", ctypes.c_size_t), ("vbart", ctypes.c_size_t),
+                ("vrow", ctypes.c_size_t), ("kbar", ctypes.c_size_t), ("vbar", ctypes.c_size_t),
                 ("head_dim_padded", ctypes.c_int32), ("nblk_padded", ctypes.c_int32),
                 ("extent_table", ctypes.c_int32)]
 
@@ -245,8 +245,6 @@ def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_
     _check(load_library().pack3d_workspace_views(index.handle, ctypes.byref(attn), ctypes.byref(vw)))
     dp, nbp = vw.head_dim_padded, vw.nblk_padded
     es = 2 if dtype == torch.bfloat16 else 4
-    tab = index.tables()
-    nblk, bvol = tab["nblk"], tab["block_tokens"]
 
     def view(off, shape, dt=dtype, esize=es):
         cnt = math.prod(shape)
@@ -255,8 +253,8 @@ def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_
     half = d // 6
     return dict(rope_table=view(vw.rope_table, (vw.extent_table, half, 2), torch.float32, 4),
                 qrot=view(vw.qrot, (b, h, n, dp)), krot=view(vw.krot, (b, h, n, dp)),
-                vt=view(vw.vt, (b, h, nblk, dp, bvol)), kbar=view(vw.kbar, (b, h, nbp, dp)),
-                vbart=view(vw.vbart, (b, h, dp, nbp)))
+                vrow=view(vw.vrow, (b, h, n, dp)), kbar=view(vw.kbar, (b, h, nbp, dp)),
+                vbar=view(vw.vbar, (b, h, nbp, dp)))
 
 
 def profile_enable(enable: bool = True):

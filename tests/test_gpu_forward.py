@@ -47,13 +47,12 @@ def test_intermediates_rope_and_pooling(name, dtype):
         kbar = oracle.pool_blocks(kr, bvol)                           # [nblk, H, D]
         vbar = oracle.pool_blocks(vc, bvol)
         gkb = views["kbar"][v].float().cpu().numpy()                  # [H, nblkp, Dp]
-        gvb = views["vbart"][v].float().cpu().numpy()                 # [H, Dp, nblkp]
+        gvb = views["vbar"][v].float().cpu().numpy()                  # [H, nblkp, Dp]
         assert np.abs(gkb[:, :nblk, :d] - kbar.transpose(1, 0, 2)).max() < tol
-        assert np.abs(gvb[:, :d, :nblk] - vbar.transpose(1, 2, 0)).max() < tol
-        assert (gkb[:, nblk:] == 0).all() and (gvb[:, :, nblk:] == 0).all()
-        gvt = views["vt"][v].float().cpu().numpy()                    # [H, nblk, Dp, bvol]
-        want = vc.reshape(nblk, bvol, w.heads, d).transpose(2, 0, 3, 1)
-        assert np.array_equal(gvt[:, :, :d, :], want)                 # V is copied exactly
+        assert np.abs(gvb[:, :nblk, :d] - vbar.transpose(1, 0, 2)).max() < tol
+        assert (gkb[:, nblk:] == 0).all() and (gvb[:, nblk:] == 0).all()
+        gv = views["vrow"][v].float().cpu().numpy().transpose(1, 0, 2)  # [N, H, Dp]
+        assert np.array_equal(gv[..., :d], vc) and (gv[..., d:] == 0).all()   # V is copied exactly
 
 
 CASES = [
