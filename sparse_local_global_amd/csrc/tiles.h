@@ -44,17 +44,23 @@ struct Src {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // LDS row tile X[64][DP] (head dim contiguous).
-//   bf16: rows of RS elements, RS = DP when DP/32 is odd, else DP + 32, so that the row
-//   stride is 16 banks modulo 32; the 16-byte chunk c of row r is stored at chunk
-//   c ^ swz(r), swz(r) = 2*((r>>1)&1) + ((r>>2)&1).  This keeps the 128-bit score reads
-//   (8 consecutive rows, one chunk) and the transpose reads (4 consecutive rows, two
-//   chunks) free of bank conflicts.
+//   bf16: rows of RS elements; the 16-byte chunk c of row r is stored at chunk
+//   c ^ swz(r).  With gfx950's 64 four-byte LDS banks a 128-bit read serves 16 lanes a
+//   cycle and a 64-bit read 32 lanes, so the score reads (16 consecutive rows, one chunk)
+//   and the transpose reads (8 consecutive rows, two chunks) are conflict-free when
+//     DP = 32, 96:  RS = DP,      swz(r) = 2*bit2(r) + bit3(r)
+//     DP = 64, 128: RS = DP + 16, swz(r) = 2*bit3(r) + bit0(r)
+//   (checked for every row and chunk by a host-side bank simulation); the row-major tile
+//   stores stay conflict-free too, except 2-way for DP = 64.
 //   fp32: rows of DP + 4 floats, no swizzle.
 template <typename T, int DP> struct TileGeom;
 template <int DP> struct TileGeom<bf16, DP> {
-  static constexpr int RS = ((DP / 32) & 1) ? DP : DP + 32;
+  static constexpr bool odd = (DP / 32) & 1;
+  static constexpr int RS = odd ? DP : DP + 16;
   static constexpr int vec = 8;
-  __device__ static inline int swz(int r) { return (((r >> 1) & 1) << 1) | ((r >> 2) & 1); }
+  __device__ static inline int swz(int r) {
+    return odd ? ((((r >> 2) & 1) << 1) | ((r >> 3) & 1)) : ((((r >> 3) & 1) << 1) | (r & 1));
+  }
   // element offset of chunk c (8 elements) of row r
   __device__ static inline int chunk(int r, int c) { return r * RS + ((c ^ swz(r)) << 3); }
 };
