@@ -183,35 +183,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float c = a.scale_log2;
   // tile t = (query block q_begin + t / tpb, sub-tile t % tpb); pipelined like the forward
   const int total = (q_end - q_begin) * tpb;
-  RowRegs<T, DP> rq, rg;
-  float pl = INFINITY, pd = 0.f;
-  auto fetch = [&](int t) {
+  struct Stage {
+    RowRegs<T, DP> q, g;
+    float lse2, delta;  // of tile row tid (tid < 64)
+  } st0, st1;
+  auto fetch = [&](Stage& S, int t) {
     const int qb = q_begin + t / tpb, qs = t - (t / tpb) * tpb;
     const int row0 = qb * bvol + qs * kTile;
     if constexpr (ONE_BLOCK) {
-      rq.fetch_at(qrot, (uint32_t)row0 * DP);
-      rg.fetch_at(doc, (uint32_t)row0 * DP);
+      S.q.fetch_at(qrot, (uint32_t)row0 * DP);
+      S.g.fetch_at(doc, (uint32_t)row0 * DP);
     } else {
-      rq.fetch(qrot, nrow, [&](int r) { return (row0 + r) * DP; });
-      rg.fetch(doc, nrow, [&](int r) { return (row0 + r) * DP; });
+      S.q.fetch(qrot, nrow, [&](int r) { return (row0 + r) * DP; });
+      S.g.fetch(doc, nrow, [&](int r) { return (row0 + r) * DP; });
     }
     if (tid < kTile) {
-      pl = tid < nrow ? a.lsec[bh * N + row0 + tid] * kLog2e : INFINITY;
-      pd = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
+      S.lse2 = tid < nrow ? a.lsec[bh * N + row0 + tid] * kLog2e : INFINITY;
+      S.delta = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
     }
   };
-  if (total > 0) fetch(0);
-  for (int t = 0; t < total; ++t) {
-    const int qb = q_begin + t / tpb;
-    __syncthreads();
-    rq.store(sm.q);
-    rg.store(sm.g);
+  auto store = [&](const Stage& S) {
+    S.q.store(sm.q);
+    S.g.store(sm.g);
     if (tid < kTile) {
-      sm.lse[tid] = pl;
-      sm.delta[tid] = pd;
+      sm.lse[tid] = S.lse2;
+      sm.delta[tid] = S.delta;
     }
-    __syncthreads();
-    if (t + 1 < total) fetch(t + 1);
+  };
+  auto compute = [&](int t) {
+    const int qb = q_begin + t / tpb;
     const int qz = qb / (nby * nbx), qy = (qb / nbx) % nby, qx = qb % nbx;
     const int cheb = max(max(abs(qz - sz), abs(qy - sy)), abs(qx - sx));
     const bool masked = sid >= a.nblk || cheb <= a.radius;
@@ -231,7 +231,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     accum(sm.g, s, dv, col, grp);
     accum(sm.q, dp, dk, col, grp);
-  }
+  };
+  pipeline2(total, st0, st1, fetch, store, compute);
   const int64_t base = (((int64_t)chunk * a.B * a.H + bh) * a.nblkp + sid) * DP;
 #pragma unroll
   for (int dt = 0; dt < DP / 16; ++dt) {
@@ -262,7 +263,7 @@ struct LocSmem {
     struct {
       RowTile<T, DP> q, g;
     } t;
-    float st[2][kTile][DP + 1];
+    float st[kTile][DP + 1];
   } u;
   float lse[kTile], delta[kTile];
   int list[kMaxSlots];
@@ -300,41 +301,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float c = a.scale_log2;
   const int nq = nloc * bvol;
   const int ntiles = (nq + kTile - 1) / kTile;
-  RowRegs<T, DP> rq, rg;
-  float pl = INFINITY, pd = 0.f;
-  auto fetch = [&](int t) {
+  struct Stage {
+    RowRegs<T, DP> q, g;
+    float lse2, delta;  // of tile row tid (tid < 64)
+  } st0, st1;
+  auto fetch = [&](Stage& S, int t) {
     const int j0 = t * kTile;
     const int valid = nq - j0 < kTile ? nq - j0 : kTile;
     const VirtualRows vr(sm.list, bvol, j0);
     if constexpr (ONE_BLOCK) {
       const int row0 = vr.blk0 * bvol + vr.off0;
-      rq.fetch_at(qrot, (uint32_t)row0 * DP);
-      rg.fetch_at(doc, (uint32_t)row0 * DP);
+      S.q.fetch_at(qrot, (uint32_t)row0 * DP);
+      S.g.fetch_at(doc, (uint32_t)row0 * DP);
     } else {
-      rq.fetch(qrot, valid, [&](int r) { return vr.row(r) * DP; });
-      rg.fetch(doc, valid, [&](int r) { return vr.row(r) * DP; });
+      S.q.fetch(qrot, valid, [&](int r) { return vr.row(r) * DP; });
+      S.g.fetch(doc, valid, [&](int r) { return vr.row(r) * DP; });
     }
     if (tid < kTile) {
-      pl = INFINITY;
-      pd = 0.f;
+      S.lse2 = INFINITY;   // padding rows: P = 0
+      S.delta = 0.f;
       if (tid < valid) {
         const int row = vr.row(tid);
-        pl = a.lsec[bh * N + row] * kLog2e;
-        pd = a.delta[bh * N + row];
+        S.lse2 = a.lsec[bh * N + row] * kLog2e;
+        S.delta = a.delta[bh * N + row];
       }
     }
   };
-  fetch(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    rq.store(sm.u.t.q);
-    rg.store(sm.u.t.g);
+  auto store = [&](const Stage& S) {
+    S.q.store(sm.u.t.q);
+    S.g.store(sm.u.t.g);
     if (tid < kTile) {
-      sm.lse[tid] = pl;
-      sm.delta[tid] = pd;
+      sm.lse[tid] = S.lse2;
+      sm.delta[tid] = S.delta;
     }
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
+  };
+  auto compute = [&](int) {
     f32x4 s[4], dp[4];
     score(sm.u.t.q, kf, s, col, grp);
     score(sm.u.t.g, vf, dp, col, grp);
@@ -350,10 +351,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     accum(sm.u.t.g, s, dv, col, grp);
     accum(sm.u.t.q, dp, dk, col, grp);
-  }
+  };
+  pipeline2(ntiles, st0, st1, fetch, store, compute);
   __syncthreads();  // the staging area below overlays the tiles
 
-  // epilogue: dK~ = scale * acc + dKbar / |b|, dV = acc + dVbar / |b|; then R^T and scatter
+  // epilogue: dK~ = scale * acc + dKbar / |b| (then R^T), dV = acc + dVbar / |b|, each
+  // staged through the same LDS rows and scattered to packed order
   const float inv = 1.0f / (float)bvol;
   const float* dkb = a.dkbar + (bh * a.nblkp + kb) * DP;
   const float* dvb = a.dvbar + (bh * a.nblkp + kb) * DP;
@@ -362,18 +365,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 16 * dt + 4 * grp + i;
-      float xk = dk[dt][i] * a.scale, xv = dv[dt][i];
-      if (a.with_summaries) {
-        xk += dkb[d] * inv;
-        xv += dvb[d] * inv;
-      }
-      sm.u.st[0][kloc][d] = xk;
-      sm.u.st[1][kloc][d] = xv;
+      sm.u.st[kloc][d] = dk[dt][i] * a.scale + (a.with_summaries ? dkb[d] * inv : 0.f);
     }
   }
   __syncthreads();
-  write_rows<T>(a, &sm.u.st[0][0][0], DP + 1, nk, b, h, krow0, true, (T*)a.dk, sm.src, sm.rel);
-  write_rows<T>(a, &sm.u.st[1][0][0], DP + 1, nk, b, h, krow0, false, (T*)a.dv, sm.src, sm.rel);
+  write_rows<T>(a, &sm.u.st[0][0], DP + 1, nk, b, h, krow0, true, (T*)a.dk, sm.src, sm.rel);
+#pragma unroll
+  for (int dt = 0; dt < DP / 16; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * dt + 4 * grp + i;
+      sm.u.st[kloc][d] = dv[dt][i] + (a.with_summaries ? dvb[d] * inv : 0.f);
+    }
+  }
+  __syncthreads();
+  write_rows<T>(a, &sm.u.st[0][0], DP + 1, nk, b, h, krow0, false, (T*)a.dv, sm.src, sm.rel);
 }
 
 // ---------------------------------------------------------------------------------
@@ -423,7 +429,7 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
 }
 
 template <typename T, int DP, bool ONE_BLOCK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dq(BwdArgs a) {
   __shared__ DqSmem<T, DP> sm;
   const int ntile = a.nblk * a.tiles_per_block;
   const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
@@ -462,33 +468,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nkeys = nloc * bvol;
   const int nlt = (nkeys + kTile - 1) / kTile;
   const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
-  RowRegs<T, DP> rk, rv;
-  auto fetch = [&](int t) {
+  struct Stage {
+    RowRegs<T, DP> k, v;
+  } st0, st1;
+  auto fetch = [&](Stage& S, int t) {
     if (t < nlt) {
       const int j0 = t * kTile;
       const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
       const VirtualRows vr(sm.list, bvol, j0);
       if constexpr (ONE_BLOCK) {
         const int row0 = vr.blk0 * bvol + vr.off0;
-        rk.fetch_at(krot, (uint32_t)row0 * DP);
-        rv.fetch_at(vrow, (uint32_t)row0 * DP);
+        S.k.fetch_at(krot, (uint32_t)row0 * DP);
+        S.v.fetch_at(vrow, (uint32_t)row0 * DP);
       } else {
-        rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
-        rv.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
+        S.k.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
+        S.v.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
       }
     } else {
       const int r0 = (t - nlt) * kTile;
-      rk.fetch_at(kbar, (uint32_t)r0 * DP);
-      rv.fetch_at(vbar, (uint32_t)r0 * DP);
+      S.k.fetch_at(kbar, (uint32_t)r0 * DP);
+      S.v.fetch_at(vbar, (uint32_t)r0 * DP);
     }
   };
-  fetch(0);
-  for (int t = 0; t < total; ++t) {
-    __syncthreads();
-    rk.store(sm.u.t.k);
-    rv.store(sm.u.t.v);
-    __syncthreads();
-    if (t + 1 < total) fetch(t + 1);
+  auto store = [&](const Stage& S) {
+    S.k.store(sm.u.t.k);
+    S.v.store(sm.u.t.v);
+  };
+  auto compute = [&](int t) {
     uint64_t live;
     if (t < nlt) {
       const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
@@ -500,7 +506,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
     dq_step(sm, qf, gf, dq, lse2, delta, c, col, grp, live);
-  }
+  };
+  pipeline2(total, st0, st1, fetch, store, compute);
   __syncthreads();  // the staging area below overlays the tiles
 #pragma unroll
   for (int dt = 0; dt < DP / 16; ++dt) {

@@ -153,28 +153,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int nlt = (nkeys + kTile - 1) / kTile;
   const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
   // two register stages: the loads of tile t+2 are issued while tile t is computed
-  RowRegs<T, DP> rk0, rk1;
-  RowRegs<T, DP> rv0, rv1;
+  struct Stage {
+    RowRegs<T, DP> k, v;
+  } st0, st1;
   const int tpk = bvol / kTile;  // tiles per block (ONE_BLOCK)
-  auto fetch = [&](RowRegs<T, DP>& rk, RowRegs<T, DP>& rv, int t) {
+  auto fetch = [&](Stage& S, int t) {
     if (t < nlt) {
       if constexpr (ONE_BLOCK) {
         const int q = t / tpk, off = (t - q * tpk) * kTile;
         const int blk = sm.list[q];
-        rk.fetch_at(krot, (uint32_t)(blk * bvol + off) * DP);
-        rv.fetch_at(vrow, (uint32_t)(blk * bvol + off) * DP);
+        S.k.fetch_at(krot, (uint32_t)(blk * bvol + off) * DP);
+        S.v.fetch_at(vrow, (uint32_t)(blk * bvol + off) * DP);
       } else {
         const int j0 = t * kTile;
         const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
         const VirtualRows vr(sm.list, bvol, j0);
-        rk.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
-        rv.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
+        S.k.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
+        S.v.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
       }
     } else {
       const int r0 = (t - nlt) * kTile;
-      rk.fetch_at(kbar, (uint32_t)r0 * DP);
-      rv.fetch_at(vbar, (uint32_t)r0 * DP);
+      S.k.fetch_at(kbar, (uint32_t)r0 * DP);
+      S.v.fetch_at(vbar, (uint32_t)r0 * DP);
     }
+  };
+  auto store = [&](const Stage& S) {
+    S.k.store(sm.k);
+    S.v.store(sm.v);
   };
   auto compute = [&](int t) {
     uint64_t live;
@@ -189,24 +194,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
     tile_step(sm, f, st, c, col, grp, live);
   };
-  fetch(rk0, rv0, 0);
-  if (total > 1) fetch(rk1, rv1, 1);
-  for (int t = 0; t < total; t += 2) {
-    __syncthreads();  // LDS free (and, at t = 0, the local-block bitmask complete)
-    rk0.store(sm.k);
-    rv0.store(sm.v);
-    __syncthreads();
-    if (t + 2 < total) fetch(rk0, rv0, t + 2);
-    compute(t);
-    if (t + 1 < total) {
-      __syncthreads();
-      rk1.store(sm.k);
-      rv1.store(sm.v);
-      __syncthreads();
-      if (t + 3 < total) fetch(rk1, rv1, t + 3);
-      compute(t + 1);
-    }
-  }
+  pipeline2(total, st0, st1, fetch, store, compute);
 
   // epilogue: o = acc / l, lse = m ln2 + ln l, scattered back to packed order
   float l = st.l;

@@ -223,6 +223,31 @@ struct RowRegs {
   }
 };
 
+// Two-stage software pipeline over tiles 0 .. total-1: the global loads of tile t+2 are
+// issued (into the stage tile t used) right after tile t is stored to LDS, so they have
+// two tile computations to land.  fetch(stage, t) issues the loads, store(stage) writes
+// the staged tile to LDS, compute(t) consumes it.  The loop is unrolled by two so each
+// stage is a named register set (no dynamically indexed registers).
+template <typename Stage, typename Fetch, typename Store, typename Compute>
+__device__ inline void pipeline2(int total, Stage& s0, Stage& s1, Fetch fetch, Store store, Compute compute) {
+  if (total > 0) fetch(s0, 0);
+  if (total > 1) fetch(s1, 1);
+  for (int t = 0; t < total; t += 2) {
+    __syncthreads();  // the previous tile's readers are done with LDS
+    store(s0);
+    __syncthreads();
+    if (t + 2 < total) fetch(s0, t + 2);
+    compute(t);
+    if (t + 1 < total) {
+      __syncthreads();
+      store(s1);
+      __syncthreads();
+      if (t + 3 < total) fetch(s1, t + 3);
+      compute(t + 1);
+    }
+  }
+}
+
 // Rows j0 .. j0+63 of the virtual concatenation of the blocks in `list` (bvol rows each,
 // canonical order).  When bvol is a multiple of 64 the tile lies inside one block and
 // every row offset follows from one base; otherwise each row finds its block.
