@@ -36,6 +36,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources, tying a stored counter measurement to the code it measured."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_local_global_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when the summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_65k.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
 def pair_counts(tables: dict) -> tuple[int, int]:
     """(local pairs, summary pairs) per (volume, head), from the neighbour table of volume 0."""
     nbr = tables["nbr"][0].cpu()
@@ -218,7 +245,7 @@ def main(argv=None) -> int:
                    "tokens_per_step": tokens, "heads": w.heads, "head_dim": d, "block_zyx": list(w.block),
                    "local_radius": w.radius, "packing": w.packing, "accumulation": "fp32"},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": dk["frac"], "traffic": None,
+                     "unit": "TFLOP/s", "frac": dk["frac"], "traffic": stored_traffic(dominant),
                      "flop_per_launch": dk["flop_per_launch"], "avg_launch_ms": dk["avg_ms"]},
         "kernels": kern,
         "forward_ms": ms_fwd,
@@ -232,6 +259,7 @@ def main(argv=None) -> int:
         "index_build_ms": index_ms,
         "ms_per_step_with_kernel_events": ms_step_profiled,
         "pairs_per_volume_head": {"local": local, "summary": summ},
+        "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         log(f"bench: timing the fp64 oracle on {args.cpu_sample_blocks} query blocks per volume")
