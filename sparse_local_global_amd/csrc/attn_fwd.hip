@@ -216,10 +216,175 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
+// ---- bf16: two wave64s per 64-query tile, 32 query columns per wave ------------------
+// v_mfma_f32_32x32x16_bf16 reads each 16-byte K / V fragment from LDS once per 32
+// query columns (half the LDS traffic per multiply of the 16-column layout), and the
+// row maximum of a query needs one cross-lane step (lanes l and l ^ 32).
+constexpr int kThreads32 = 128;
+
+template <int DP>
+struct State32 {
+  f32x16 o[DP / 32];
+  float m, l;
+};
+
+template <int DP>
+__device__ inline void tile_step32(const FwdSmem<bf16, DP>& sm, const ColFrag32<DP>& f, State32<DP>& st, float c,
+                                   int lane, int half, uint64_t live) {
+  const int col = lane & 31;
+  f32x16 s[2];
+  score32(sm.k, f, s, col, half);
+  if (live != ~0ull) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * mt + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (!((live >> r) & 1ull)) s[mt][i] = -INFINITY;
+      }
+    }
+  }
+  float m0 = s[0][0], m1 = s[1][0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    m0 = fmaxf(m0, s[0][i]);
+    m1 = fmaxf(m1, s[1][i]);
+  }
+  float mx = fmaxf(m0, m1);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx *= c;  // scale > 0: the maximum of the scaled logits
+  if (mx > st.m + kRescale) {
+    const float alpha = fast_exp2(st.m - mx);
+    st.m = mx;
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) st.o[dt] *= alpha;
+  }
+  const float mneg = -st.m;
+  float ls = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(s[mt][i], c, mneg));
+      s[mt][i] = p;
+      ls += p;
+    }
+  }
+  st.l += ls;
+  accum32(sm.v, s, st.o, lane, half);
+}
+
+template <int DP, bool ONE_BLOCK>
+__global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_fwd32(FwdArgs a) {
+  __shared__ FwdSmem<bf16, DP> sm;
+  const int ntile = a.nblk * a.tiles_per_block;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
+  const int qb = tile / a.tiles_per_block, qsub = tile - qb * a.tiles_per_block;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int N = a.N, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int nq = bvol < kTile ? bvol : kTile;
+  const int qrow0 = qb * bvol + qsub * kTile;
+  const int mask_words = a.nblkp / 32;
+
+  for (int i = tid; i < mask_words; i += kThreads32) sm.mask[i] = 0u;
+  if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
+  __syncthreads();
+  const int nloc = sm.nloc;
+  for (int i = tid; i < nloc; i += kThreads32) atomicOr(&sm.mask[sm.list[i] >> 5], 1u << (sm.list[i] & 31));
+
+  const int qloc = 32 * wave + col;
+  ColFrag32<DP> f;
+  f.load((const bf16*)a.qrot + (bh * N + qrow0 + qloc) * DP, qloc < nq, half);
+  State32<DP> st;
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) st.o[dt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const float c = a.scale_log2;
+
+  const size_t es = sizeof(bf16);
+  const Src krot((const bf16*)a.krot + bh * N * DP, (size_t)N * DP * es);
+  const Src vrow((const bf16*)a.vr + bh * N * DP, (size_t)N * DP * es);
+  const Src kbar((const bf16*)a.kbar + bh * a.nblkp * DP, (size_t)a.nblkp * DP * es);
+  const Src vbar((const bf16*)a.vbar + bh * a.nblkp * DP, (size_t)a.nblkp * DP * es);
+  const int nkeys = nloc * bvol;
+  const int nlt = (nkeys + kTile - 1) / kTile;
+  const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
+  struct Stage {
+    RowRegs<bf16, DP, kThreads32> k, v;
+  } st0;
+  const int tpk = bvol / kTile;
+  auto fetch = [&](Stage& S, int t) {
+    if (t < nlt) {
+      if constexpr (ONE_BLOCK) {
+        const int q = t / tpk, off = (t - q * tpk) * kTile;
+        const int blk = sm.list[q];
+        S.k.fetch_at(krot, (uint32_t)(blk * bvol + off) * DP);
+        S.v.fetch_at(vrow, (uint32_t)(blk * bvol + off) * DP);
+      } else {
+        const int j0 = t * kTile;
+        const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
+        const VirtualRows vr(sm.list, bvol, j0);
+        S.k.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
+        S.v.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
+      }
+    } else {
+      const int r0 = (t - nlt) * kTile;
+      S.k.fetch_at(kbar, (uint32_t)r0 * DP);
+      S.v.fetch_at(vbar, (uint32_t)r0 * DP);
+    }
+  };
+  auto store = [&](const Stage& S) {
+    S.k.store(sm.k);
+    S.v.store(sm.v);
+  };
+  auto compute = [&](int t) {
+    uint64_t live;
+    if (t < nlt) {
+      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
+      live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+    } else {
+      const int ts = t - nlt, r0 = ts * kTile;
+      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
+      const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
+      live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
+    }
+    tile_step32(sm, f, st, c, lane, half, live);
+  };
+  pipeline1(total, st0, fetch, store, compute);
+
+  // epilogue: o = acc / l, lse = m ln2 + ln l, scattered back to packed order
+  float l = st.l + __shfl_xor(st.l, 32);
+  if (qloc < nq) {
+    const int src = a.perm[(int64_t)b * N + qrow0 + qloc];
+    const float inv = 1.0f / l;
+    bf16* orow = (bf16*)a.out + (((int64_t)b * N + src) * a.H + h) * a.D;
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (d < a.D) orow[d] = (bf16)(st.o[dt][i] * inv);
+      }
+    }
+    if (half == 0) a.lse[bh * N + src] = st.m * kLn2 + logf(l);
+  }
+}
+
 template <typename T, int DP>
 void launch_dp(const Dims& d, const FwdArgs& a, dim3 grid, hipStream_t s) {
-  if (d.bvol % kTile == 0) hipLaunchKernelGGL((k_attn_fwd<T, DP, true>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_attn_fwd<T, DP, false>), grid, dim3(kThreads), 0, s, a);
+  // 32-column waves for bf16 up to Dp = 96 (at Dp = 128 their registers would spill)
+  if constexpr (sizeof(T) == 2 && DP <= 96) {
+    if (d.bvol % kTile == 0) hipLaunchKernelGGL((k_attn_fwd32<DP, true>), grid, dim3(kThreads32), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_fwd32<DP, false>), grid, dim3(kThreads32), 0, s, a);
+  } else {
+    if (d.bvol % kTile == 0) hipLaunchKernelGGL((k_attn_fwd<T, DP, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_fwd<T, DP, false>), grid, dim3(kThreads), 0, s, a);
+  }
 }
 
 template <typename T>

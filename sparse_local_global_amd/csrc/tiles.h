@@ -181,23 +181,81 @@ __device__ inline void accum(const RowTile<float, DP>& t, const f32x4 (&p)[4], f
   }
 }
 
+// ---- 32-column waves (bf16): v_mfma_f32_32x32x16_bf16 ------------------------------
+// A wave owns 32 columns (lane & 31) and the two lane halves h = lane >> 5 split every
+// 16-wide contraction step: k slot e of half h is head dim 16s + 8h + e (score) or row
+// 16s + 4h + e (e < 4) / 16s + 8 + 4h + (e - 4) (e >= 4) (accum).  A 32x32 accumulator
+// holds element (row 8*(i/4) + 4h + i%4, column lane & 31) in slot i.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+template <int DP> struct ColFrag32 {
+  bf16x8 b[DP / 16];
+  __device__ inline void load(const bf16* __restrict__ row, bool ok, int half) {
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s) {
+      if (ok) b[s] = *(const bf16x8*)(row + 16 * s + 8 * half);
+      else b[s] = bf16x8{};
+    }
+  }
+};
+
+// s[mt][i] = score of tile row 32mt + 8(i/4) + 4h + i%4 against column (lane & 31)
+template <int DP>
+__device__ inline void score32(const RowTile<bf16, DP>& t, const ColFrag32<DP>& f, f32x16 (&s)[2], int col, int half) {
+  using G = TileGeom<bf16, DP>;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int k = 0; k < DP / 16; ++k) {
+      const bf16x8 a = *(const bf16x8*)&t.x[G::chunk(32 * mt + col, 2 * k + half)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.b[k], acc, 0, 0, 0);
+    }
+    s[mt] = acc;
+  }
+}
+
+// acc[dt][i] += sum_r X[r][32dt + 8(i/4) + 4h + i%4] * p[r][lane & 31]
+template <int DP>
+__device__ inline void accum32(const RowTile<bf16, DP>& t, const f32x16 (&p)[2], f32x16 (&acc)[DP / 32], int lane,
+                               int half) {
+  const int lane16 = lane & 15, hi16 = (lane >> 4) & 1;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    // rows 16s + 4h + e (e < 4) and 16s + 8 + 4h + (e - 4): accumulator slots 8(s%2) + e
+    const f32x16& ps = p[s >> 1];
+    const int i0 = 8 * (s & 1);
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (bf16)ps[i0 + e];
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) {
+      const int c0 = 32 * dt + 16 * hi16;
+      const bf16x4 lo = read_column4(t, 16 * s + 4 * half, c0, lane16);
+      const bf16x4 hi = read_column4(t, 16 * s + 8 + 4 * half, c0, lane16);
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
+    }
+  }
+}
+
 // Register-staged tile copies, for a software pipeline: fetch() issues every 16-byte
 // global load of a tile at once (no dependency between them), store() writes them to
 // LDS later, so the loads of a later tile are in flight while the current one is
 // computed.
-template <typename T, int DP>
+template <typename T, int DP, int NT = kThreads>
 struct RowRegs {
   using G = TileGeom<T, DP>;
   static constexpr int V = G::vec;
-  static constexpr int n = kTile * DP / V / kThreads;
-  static_assert(kTile * DP / V % kThreads == 0, "tile chunks must spread evenly");
+  static constexpr int n = kTile * DP / V / NT;
+  static_assert(kTile * DP / V % NT == 0, "tile chunks must spread evenly");
   uint4 r[n];
   // rowoff(r) = element offset of row r (r < valid); rows past `valid` read zero
   template <typename RowOff>
   __device__ inline void fetch(const Src& src, int valid, RowOff rowoff) {
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-      const int c = threadIdx.x + i * kThreads;
+      const int c = threadIdx.x + i * NT;
       const int row = c / (DP / V), cc = (c - row * (DP / V)) * V;
       // rows past `valid` read past the end of the buffer, which returns zero
       const uint32_t off = row < valid ? (uint32_t)(rowoff(row) + cc) * (uint32_t)sizeof(T) : 0x80000000u;
@@ -209,14 +267,14 @@ struct RowRegs {
     const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base * (uint32_t)sizeof(T)));
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-      const int c = threadIdx.x + i * kThreads;
+      const int c = threadIdx.x + i * NT;
       r[i] = src.load16(b + (uint32_t)c * (uint32_t)(V * sizeof(T)));  // row-major: chunk c at c * V
     }
   }
   __device__ inline void store(RowTile<T, DP>& t) const {
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-      const int c = threadIdx.x + i * kThreads;
+      const int c = threadIdx.x + i * NT;
       const int row = c / (DP / V), ch = c - row * (DP / V);
       *(uint4*)&t.x[G::chunk(row, ch)] = r[i];
     }
@@ -245,6 +303,19 @@ __device__ inline void pipeline2(int total, Stage& s0, Stage& s1, Fetch fetch, S
       if (t + 3 < total) fetch(s1, t + 3);
       compute(t + 1);
     }
+  }
+}
+
+// One-stage variant: the loads of tile t+1 are issued right after tile t is stored.
+template <typename Stage, typename Fetch, typename Store, typename Compute>
+__device__ inline void pipeline1(int total, Stage& s0, Fetch fetch, Store store, Compute compute) {
+  if (total > 0) fetch(s0, 0);
+  for (int t = 0; t < total; ++t) {
+    __syncthreads();
+    store(s0);
+    __syncthreads();
+    if (t + 1 < total) fetch(s0, t + 1);
+    compute(t);
   }
 }
 
