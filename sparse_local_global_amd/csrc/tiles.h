@@ -102,15 +102,16 @@ template <int DP> struct ColFrag<float, DP> {
 template <int DP>
 __device__ inline void score(const RowTile<bf16, DP>& t, const ColFrag<bf16, DP>& f, f32x4 (&s)[4], int col, int grp) {
   using G = TileGeom<bf16, DP>;
+  // k outer, row tile inner: the four accumulation chains interleave
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < DP / 32; ++k) {
+  for (int k = 0; k < DP / 32; ++k) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
       const bf16x8 a = *(const bf16x8*)&t.x[G::chunk(16 * mt + col, 4 * k + grp)];
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, f.b[k], acc, 0, 0, 0);
+      s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, f.b[k], s[mt], 0, 0, 0);
     }
-    s[mt] = acc;
   }
 }
 
@@ -203,15 +204,16 @@ template <int DP> struct ColFrag32 {
 template <int DP>
 __device__ inline void score32(const RowTile<bf16, DP>& t, const ColFrag32<DP>& f, f32x16 (&s)[2], int col, int half) {
   using G = TileGeom<bf16, DP>;
+  // k outer, row tile inner: the two accumulation chains interleave
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    f32x16 acc = {};
+  for (int k = 0; k < DP / 16; ++k) {
 #pragma unroll
-    for (int k = 0; k < DP / 16; ++k) {
+    for (int mt = 0; mt < 2; ++mt) {
       const bf16x8 a = *(const bf16x8*)&t.x[G::chunk(32 * mt + col, 2 * k + half)];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.b[k], acc, 0, 0, 0);
+      s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.b[k], s[mt], 0, 0, 0);
     }
-    s[mt] = acc;
   }
 }
 
