@@ -11,7 +11,7 @@
 //   dq = R(c)^T dQ~, dk = R(c)^T dK~  (R orthogonal; the mean broadcasts 1/|b| to each member).
 //
 // Kernels, in launch order (no atomics anywhere, so results are bitwise reproducible):
-//   bwd_pre      per block: delta, dO and lse gathered to canonical order
+//   bwd_pre      per block: delta, dO and lse (in log2 units) gathered to canonical order
 //   bwd_summary  summary-major: each workgroup owns 64 summaries of one (volume, head) and a
 //                chunk of query blocks; masks the summaries local to each query block and
 //                accumulates partial dKbar, dVbar (fp32) per chunk
@@ -35,7 +35,7 @@ namespace {
 struct BwdArgs {
   // forward intermediates and backward layouts (workspace, canonical order)
   const void* qrot; const void* krot; const void* vr; const void* kbar; const void* vbar;
-  void* doc; float* lsec; float* delta;
+  void* doc; float* lsec; float* delta;   // lsec: lse * log2(e), canonical order
   float* dkbar; float* dvbar; float* part_k; float* part_v;
   const float2* tab;
   // caller buffers (packed order)
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
       float s = 0.f;
       for (int c = 0; c < nch; ++c) s += part[tid * nch + c];
       a.delta[bh * N + kappa] = s;
-      a.lsec[bh * N + kappa] = a.lse[bh * N + src];
+      a.lsec[bh * N + kappa] = a.lse[bh * N + src] * kLog2e;   // log2 units
     }
     __syncthreads();
   }
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       S.g.fetch(doc, nrow, [&](int r) { return (row0 + r) * DP; });
     }
     if (tid < kTile) {
-      S.lse2 = tid < nrow ? a.lsec[bh * N + row0 + tid] * kLog2e : INFINITY;
+      S.lse2 = tid < nrow ? a.lsec[bh * N + row0 + tid] : INFINITY;
       S.delta = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
     }
   };
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       S.delta = 0.f;
       if (tid < valid) {
         const int row = vr.row(tid);
-        S.lse2 = a.lsec[bh * N + row] * kLog2e;
+        S.lse2 = a.lsec[bh * N + row];
         S.delta = a.delta[bh * N + row];
       }
     }
@@ -380,6 +380,180 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   __syncthreads();
   write_rows<T>(a, &sm.u.st[0][0], DP + 1, nk, b, h, krow0, false, (T*)a.dv, sm.src, sm.rel);
+}
+
+// ---------------------------------------------------------------------------------
+// bwd_local for bf16 with 32 key columns per wave, fed by direct LDS copies.
+// Workgroup = (64 keys, head, volume) as above, four waves: key half kh = wave & 1 and
+// query-row half qh = wave >> 1 of every query tile; the two query halves' partial
+// dK~, dV are summed through LDS before the epilogue.  v_mfma_f32_32x32x16_bf16 halves
+// the LDS reads per multiply against 16-column waves, and the copies (query tile, dO
+// tile, lse, delta) hold no registers, so three LDS stages keep two tiles in flight.
+// Rows past the end of the last tile arrive as zeros: Q = dO = 0 there, so their
+// probabilities multiply zero rows and add nothing.
+// ---------------------------------------------------------------------------------
+constexpr int kLdsStages = 3;
+
+template <int DP>
+struct LocStage32 {
+  RowTile<bf16, DP> q, g;
+  float lse2[kTile], delta[kTile];
+};
+
+template <int DP>
+struct LocSmem32 {
+  int list[kMaxSlots];
+  int nloc;
+  int src[kTile], rel[kTile * 3];
+};
+
+// Direct copy of lse2 / delta for tile rows 16 w .. 16 w + 15 (lanes 0..15 of wave w).
+__device__ inline void issue_rows16(const Src& src, float* dst16, uint32_t byte_off) {
+  if ((threadIdx.x & 63) < 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_void*)dst16, 4, byte_off, 0, 0, 0);
+}
+
+template <int DP, bool ONE_BLOCK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_local32(BwdArgs a) {
+  __shared__ LocSmem32<DP> sm;
+  // one LDS object per stage; the epilogue reuses them: query half 1's partial dK~, dV
+  // for key half 0 / 1 in stages 0 / 1 ([slot][lane] float4s), the staging rows in stage 2
+  __shared__ LocStage32<DP> s0, s1, s2;
+  static_assert(sizeof(f32x4) * DP / 32 * 8 * 64 <= sizeof(LocStage32<DP>), "partials fit a stage");
+  static_assert(sizeof(float) * kTile * (DP + 1) <= sizeof(LocStage32<DP>), "staging rows fit a stage");
+  const int ntile = a.nblk * a.tiles_per_block;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
+  const int kb = tile / a.tiles_per_block, ks = tile - kb * a.tiles_per_block;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int N = a.N, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int nk = bvol < kTile ? bvol : kTile;
+  const int krow0 = kb * bvol + ks * kTile;
+  const int kloc = 32 * kh + col;
+  ColFrag32<DP> kf, vf;
+  kf.load((const bf16*)a.krot + (bh * N + krow0 + kloc) * DP, kloc < nk, half);
+  vf.load((const bf16*)a.vr + (bh * N + krow0 + kloc) * DP, kloc < nk, half);
+  if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + kb) * a.slots, a.slots, sm.list, &sm.nloc);
+  __syncthreads();
+  const int nloc = sm.nloc;
+  f32x16 dk[DP / 32], dv[DP / 32];
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) dk[dt] = dv[dt] = f32x16{};
+
+  const size_t slice = (size_t)N * DP * sizeof(bf16);
+  const Src qrot((const bf16*)a.qrot + bh * N * DP, slice);
+  const Src doc((const bf16*)a.doc + bh * N * DP, slice);
+  const Src lsec(a.lsec + bh * N, (size_t)N * sizeof(float));
+  const Src dlt(a.delta + bh * N, (size_t)N * sizeof(float));
+  const float c = a.scale_log2;
+  const int nq = nloc * bvol;
+  const int ntiles = (nq + kTile - 1) / kTile;
+  using Dma = TileDma<DP, kThreads>;
+  const Dma dma;
+  auto stage = [&](auto st) -> LocStage32<DP>& {
+    if constexpr (decltype(st)::value == 0) return s0;
+    else if constexpr (decltype(st)::value == 1) return s1;
+    else return s2;
+  };
+  auto issue = [&](auto st, int t) {
+    LocStage32<DP>& S = stage(st);
+    const int j0 = t * kTile;
+    const VirtualRows vr(sm.list, bvol, j0);
+    const int w = wave_id(), r = 16 * w + (lane & 15);
+    if constexpr (ONE_BLOCK) {
+      const int row0 = vr.blk0 * bvol + vr.off0;
+      dma.issue_at(qrot, S.q, (uint32_t)row0 * DP);
+      dma.issue_at(doc, S.g, (uint32_t)row0 * DP);
+      issue_rows16(lsec, &S.lse2[16 * w], (uint32_t)(row0 + r) * 4u);
+      issue_rows16(dlt, &S.delta[16 * w], (uint32_t)(row0 + r) * 4u);
+    } else {
+      const int valid = nq - j0 < kTile ? nq - j0 : kTile;
+      dma.issue(qrot, S.q, valid, [&](int rr) { return vr.row(rr) * DP; });
+      dma.issue(doc, S.g, valid, [&](int rr) { return vr.row(rr) * DP; });
+      const uint32_t off = r < valid ? (uint32_t)vr.row(r) * 4u : 0x80000000u;
+      issue_rows16(lsec, &S.lse2[16 * w], off);
+      issue_rows16(dlt, &S.delta[16 * w], off);
+    }
+  };
+  auto compute = [&](auto st, int) {
+    const LocStage32<DP>& S = stage(st);
+    f32x16 s, dp;
+    score32_pair(S.q, kf, s, S.g, vf, dp, col, half, qh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // slots 4j .. 4j+3: rows 32qh + 8j + 4half + e
+      const f32x4 l4 = *(const f32x4*)&S.lse2[32 * qh + 8 * j + 4 * half];
+      const f32x4 d4 = *(const f32x4*)&S.delta[32 * qh + 8 * j + 4 * half];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = fast_exp2(fmaf(s[4 * j + e], c, -l4[e]));
+        s[4 * j + e] = p;
+        dp[4 * j + e] = p * (dp[4 * j + e] - d4[e]);
+      }
+    }
+    accum32_rows(S.g, s, dv, lane, half, qh);
+    accum32_rows(S.q, dp, dk, lane, half, qh);
+  };
+  pipeline_lds<kLdsStages, 2 * Dma::ROUNDS + 2>(ntiles, issue, compute);
+  __syncthreads();  // the partial and staging buffers overlay the stages
+
+  constexpr int NDT = DP / 32;
+  f32x4* part = (f32x4*)(kh == 0 ? (void*)&s0 : (void*)&s1);  // [slot][lane]
+  float(*st)[DP + 1] = (float(*)[DP + 1]) & s2;
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        part[(4 * dt + q) * 64 + lane] = f32x4{dk[dt][4 * q], dk[dt][4 * q + 1], dk[dt][4 * q + 2], dk[dt][4 * q + 3]};
+        part[(4 * NDT + 4 * dt + q) * 64 + lane] =
+            f32x4{dv[dt][4 * q], dv[dt][4 * q + 1], dv[dt][4 * q + 2], dv[dt][4 * q + 3]};
+      }
+    }
+  }
+  __syncthreads();
+  // epilogue (query half 0 holds the totals): dK~ = scale * acc + dKbar / |b| (then R^T),
+  // dV = acc + dVbar / |b|, each staged through LDS rows and scattered to packed order
+  const float inv = 1.0f / (float)bvol;
+  const float* dkb = a.dkbar + (bh * a.nblkp + kb) * DP;
+  const float* dvb = a.dvbar + (bh * a.nblkp + kb) * DP;
+  if (qh == 0) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 pk = part[(4 * dt + q) * 64 + lane];
+        const f32x4 pv = part[(4 * NDT + 4 * dt + q) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dk[dt][4 * q + e] += pk[e];
+          dv[dt][4 * q + e] += pv[e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3);
+        st[kloc][d] = dk[dt][i] * a.scale + (a.with_summaries ? dkb[d] * inv : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+  write_rows<bf16>(a, &st[0][0], DP + 1, nk, b, h, krow0, true, (bf16*)a.dk, sm.src, sm.rel);
+  if (qh == 0) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3);
+        st[kloc][d] = dv[dt][i] + (a.with_summaries ? dvb[d] * inv : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+  write_rows<bf16>(a, &st[0][0], DP + 1, nk, b, h, krow0, false, (bf16*)a.dv, sm.src, sm.rel);
 }
 
 // ---------------------------------------------------------------------------------
@@ -446,7 +620,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   ColFrag<T, DP> qf, gf;
   qf.load((const T*)a.qrot + (bh * N + qrow0 + qloc) * DP, qok, grp);
   gf.load((const T*)a.doc + (bh * N + qrow0 + qloc) * DP, qok, grp);
-  const float lse2 = qok ? a.lsec[bh * N + qrow0 + qloc] * kLog2e : INFINITY;
+  const float lse2 = qok ? a.lsec[bh * N + qrow0 + qloc] : INFINITY;
   const float delta = qok ? a.delta[bh * N + qrow0 + qloc] : 0.f;
 
   const int mask_words = a.nblkp / 32;
@@ -556,7 +730,7 @@ __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2)))
   ColFrag32<DP> qf, gf;
   qf.load((const bf16*)a.qrot + (bh * N + qrow0 + qloc) * DP, qok, half);
   gf.load((const bf16*)a.doc + (bh * N + qrow0 + qloc) * DP, qok, half);
-  const float lse2 = qok ? a.lsec[bh * N + qrow0 + qloc] * kLog2e : INFINITY;
+  const float lse2 = qok ? a.lsec[bh * N + qrow0 + qloc] : INFINITY;
   const float delta = qok ? a.delta[bh * N + qrow0 + qloc] : 0.f;
 
   const int mask_words = a.nblkp / 32;
@@ -657,7 +831,11 @@ pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   }
   {
     ProfileScope prof("bwd_local", s);
-    hipLaunchKernelGGL((k_bwd_local<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
+    // 32-column waves with direct LDS copies for bf16 where rows need no padding
+    if constexpr (sizeof(T) == 2 && (DP == 32 || DP == 96))
+      hipLaunchKernelGGL((k_bwd_local32<DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_local<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
   }
   {
     ProfileScope prof("bwd_dq", s);

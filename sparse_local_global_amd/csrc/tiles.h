@@ -19,6 +19,8 @@
 //         index g is row 16mt + 4g + i (one MFMA per i, A read as single dwords).
 #pragma once
 
+#include <type_traits>
+
 #include "layout.h"
 
 namespace pack3d {
@@ -265,6 +267,159 @@ __device__ inline void accum32(const RowTile<bf16, DP>& t, const f32x16 (&p)[2],
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
     }
+  }
+}
+
+// One 32-row block (rows 32mt .. 32mt+31) of two independent score tiles at once
+// (the two accumulation chains interleave): s1 from t1 and f1, s2 from t2 and f2,
+// slot i = row 32mt + 8(i/4) + 4h + i%4 against column (lane & 31).
+template <int DP>
+__device__ inline void score32_pair(const RowTile<bf16, DP>& t1, const ColFrag32<DP>& f1, f32x16& s1,
+                                    const RowTile<bf16, DP>& t2, const ColFrag32<DP>& f2, f32x16& s2, int col,
+                                    int half, int mt) {
+  using G = TileGeom<bf16, DP>;
+  const int be = G::base(col & 15, half) + G::off(col & 16, 0);
+  const int bo = G::base(col & 15, 2 + half) + G::off(col & 16, 0);
+  s1 = f32x16{};
+  s2 = f32x16{};
+#pragma unroll
+  for (int k = 0; k < DP / 16; ++k) {
+    const int o = (k & 1 ? bo : be) + G::off(32 * mt, 4 * (k >> 1));
+    const bf16x8 a1 = *(const bf16x8*)(t1.x + o);
+    const bf16x8 a2 = *(const bf16x8*)(t2.x + o);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, f1.b[k], s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, f2.b[k], s2, 0, 0, 0);
+  }
+}
+
+// acc[dt][i] += sum over rows r of block mt of X[r][32dt + 8(i/4) + 4h + i%4] * p[r][lane & 31],
+// p in the slot layout of score32_pair.
+template <int DP>
+__device__ inline void accum32_rows(const RowTile<bf16, DP>& t, const f32x16& p, f32x16 (&acc)[DP / 32], int lane,
+                                    int half, int mt) {
+  using G = TileGeom<bf16, DP>;
+  const int lane16 = lane & 15, hi16 = (lane >> 4) & 1;
+  const ColumnBases c0 = column_bases(t, 4 * half, lane16), c8 = column_bases(t, 8 + 4 * half, lane16);
+  const bf16* p0 = hi16 ? c0.odd : c0.even;
+  const bf16* p8 = hi16 ? c8.odd : c8.even;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    // rows 32mt + 16s + 4h + e (e < 4) and 32mt + 16s + 8 + 4h + (e - 4): slots 8s + e
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (bf16)p[8 * s + e];
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) {
+      const bf16x4 lo = read_tr(p0 + G::off(32 * mt + 16 * s, 4 * dt));
+      const bf16x4 hi = read_tr(p8 + G::off(32 * mt + 16 * s, 4 * dt));
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
+    }
+  }
+}
+
+// ---- direct global -> LDS copies ------------------------------------------------------
+// buffer_load_dwordx4 ... lds writes the 16 bytes lane l loads to LDS address
+// M0 + 16 l (dword size: M0 + 4 l), and an out-of-range load writes zeros.  One wave
+// instruction therefore fills 64 consecutive 16-byte slots of a tile: slot p of a
+// RowTile holds row p / CH, stored chunk p % CH, i.e. logical chunk (p % CH) ^ swz(row),
+// and each lane loads exactly that chunk.  No registers hold tile data, so the copies of
+// later tiles stay in flight while the current one is used.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Wait until at most n vector-memory instructions of this wave are outstanding.
+template <int n>
+__device__ inline void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Barrier between the steps of a direct-copy pipeline, where waves only read LDS and
+// copies are in flight.  No release fence: one would wait for every outstanding copy,
+// later tiles' included.  The copies the next step needs are waited for explicitly
+// (wait_vm) before it, this wave's LDS reads are complete (lgkmcnt(0)) so a stage can
+// be overwritten once every wave has passed, and the acquire fence keeps later LDS
+// reads below the barrier.
+__device__ inline void barrier_copies() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int DP, int NT>
+struct TileDma {
+  using G = TileGeom<bf16, DP>;
+  static constexpr int CH = G::RS / 8;
+  static_assert(G::RS == DP, "direct copies need unpadded rows");
+  static_assert(kTile * CH % NT == 0, "tile slots must spread evenly over the threads");
+  static constexpr int ROUNDS = kTile * CH / NT;  // vector-memory instructions per tile and wave
+  int row[ROUNDS];   // tile row of this lane's slot in round i
+  int loff[ROUNDS];  // element offset of that slot's logical chunk in a dense [64][DP] tile
+  __device__ inline TileDma() {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int p = i * NT + (int)threadIdx.x;  // = (i * NT / 64 + wave) * 64 + lane
+      const int r = p / CH, c = (p - r * CH) ^ G::swz(r);
+      row[i] = r;
+      loff[i] = r * DP + (c << 3);
+    }
+  }
+  __device__ static inline lds_void* dst(RowTile<bf16, DP>& t, int i, int w) {
+    return (lds_void*)((lds_char*)t.x + (i * NT + 64 * w) * 16);
+  }
+  // Tile rows contiguous from element `base` of src (the same on every lane); all rows valid.
+  __device__ inline void issue_at(const Src& src, RowTile<bf16, DP>& t, uint32_t base) const {
+    const int w = wave_id();
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base * 2u));
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, dst(t, i, w), 16, b + (uint32_t)loff[i] * 2u, 0, 0, 0);
+  }
+  // Row r from element offset rowoff(r) of src (r < valid); rows past `valid` become zero.
+  template <typename RowOff>
+  __device__ inline void issue(const Src& src, RowTile<bf16, DP>& t, int valid, RowOff rowoff) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int r = row[i];
+      const uint32_t off = r < valid ? (uint32_t)(rowoff(r) + loff[i] - r * DP) * 2u : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, dst(t, i, w), 16, off, 0, 0, 0);
+    }
+  }
+};
+
+template <int S> using Stage_ = std::integral_constant<int, S>;
+
+// NS-stage pipeline over tiles 0 .. total-1 that arrive by direct LDS copies:
+// issue(Stage_<s>{}, t) starts the copies of tile t into LDS stage s, and every wave
+// issues exactly PER_TILE vector-memory instructions in it; compute(Stage_<s>{}, t) uses
+// the tile.  Tile t lives in stage t % NS; stages are compile-time constants (the loop
+// is unrolled NS times), so each stage can be its own LDS object, which lets the
+// compiler see that reading one stage does not depend on copies into another.  Tile
+// t + NS - 1 is issued right after the barrier that follows every wave's compute(t - 1),
+// whose stage it reuses; tiles t+1 .. t+NS-2 stay in flight meanwhile.
+template <int NS, int PER_TILE, int S, typename Issue, typename Compute>
+__device__ inline void pipeline_step(int t, int total, Issue& issue, Compute& compute) {
+  if (NS == 3 && t + 1 < total) wait_vm<PER_TILE>();
+  else wait_vm<0>();
+  barrier_copies();
+  if (t + NS - 1 < total) issue(Stage_<(S + NS - 1) % NS>{}, t + NS - 1);
+  compute(Stage_<S>{}, t);
+}
+
+template <int NS, int PER_TILE, typename Issue, typename Compute>
+__device__ inline void pipeline_lds(int total, Issue issue, Compute compute) {
+  static_assert(NS == 2 || NS == 3, "two or three stages");
+  if (total > 0) issue(Stage_<0>{}, 0);
+  if (NS == 3 && total > 1) issue(Stage_<1>{}, 1);
+  for (int t = 0; t < total; t += NS) {
+    pipeline_step<NS, PER_TILE, 0>(t, total, issue, compute);
+    if (t + 1 < total) pipeline_step<NS, PER_TILE, 1>(t + 1, total, issue, compute);
+    if constexpr (NS == 3)
+      if (t + 2 < total) pipeline_step<NS, PER_TILE, 2>(t + 2, total, issue, compute);
   }
 }
 
