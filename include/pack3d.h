@@ -154,13 +154,21 @@ pack3d_status pack3d_forward(const pack3d_index* index, const pack3d_attn* attn,
 
 /* Backward of sum(out * dout): gradients dq, dk, dv [B, N, H, D] (attn->dtype) with
  * respect to the unrotated q, k, v, through the RoPE and the block mean pooling.
- * out_dev and lse_dev are the forward's outputs for the same inputs. */
+ * out_dev and lse_dev are the forward's outputs for the same inputs.  The workspace
+ * needs pack3d_workspace_bytes(index, attn, 1) bytes; its first
+ * pack3d_workspace_bytes(index, attn, 0) bytes have the forward's layout.
+ * reuse_forward = 0: the rotated and pooled operands are recomputed from q, k, v.
+ * reuse_forward = 1: the caller guarantees that those first bytes still hold what
+ * pack3d_forward wrote for the same index, attn, q, k, v and coords (same workspace
+ * pointer, untouched since), and the recomputation is skipped; results are then
+ * bitwise equal to reuse_forward = 0.  A broken guarantee gives wrong gradients but
+ * no out-of-bounds access.  Other values: PACK3D_E_INVALID. */
 pack3d_status pack3d_backward(const pack3d_index* index, const pack3d_attn* attn,
                               const void* q_dev, const void* k_dev, const void* v_dev,
                               const int32_t* coords_dev, const void* out_dev,
                               const float* lse_dev, const void* dout_dev, void* dq_dev,
                               void* dk_dev, void* dv_dev, void* workspace_dev,
-                              size_t workspace_bytes, void* stream);
+                              size_t workspace_bytes, int32_t reuse_forward, void* stream);
 
 /* Where the forward leaves its intermediates inside the workspace (byte offsets),
  * for inspection by tests.  All arrays are in canonical order (block-major, raster

@@ -57,7 +57,7 @@ using namespace pack3d;
 
 extern "C" const char* pack3d_last_error(void) { return g_msg; }
 
-extern "C" int32_t pack3d_version(void) { return 100; }
+extern "C" int32_t pack3d_version(void) { return 101; }
 
 extern "C" size_t pack3d_workspace_bytes(const pack3d_index* ix, const pack3d_attn* at, int for_backward) {
   if (check_attn(ix, at, "workspace_bytes") != PACK3D_OK) return 0;
@@ -99,7 +99,8 @@ extern "C" pack3d_status pack3d_forward(const pack3d_index* ix, const pack3d_att
 extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_attn* at, const void* q,
                                          const void* k, const void* v, const int32_t* coords,
                                          const void* out, const float* lse, const void* dout, void* dq,
-                                         void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+                                         void* dk, void* dv, void* ws, size_t ws_bytes, int32_t reuse_forward,
+                                         void* stream) {
   pack3d_status st = check_attn(ix, at, "backward");
   if (st != PACK3D_OK) return st;
   if (!q || !k || !v || !coords || !out || !lse || !dout || !dq || !dk || !dv || !ws)
@@ -110,9 +111,13 @@ extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_at
   Workspace w = workspace_layout(d);
   if (ws_bytes < w.bwd_total)
     return set_error(PACK3D_E_WORKSPACE, "backward: workspace %zu bytes < %zu needed", ws_bytes, w.bwd_total);
+  if (reuse_forward != 0 && reuse_forward != 1)
+    return set_error(PACK3D_E_INVALID, "backward: reuse_forward must be 0 or 1");
   hipStream_t s = (hipStream_t)stream;
-  // recompute the rotated and pooled operands (the backward is stateless)
-  st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, "rope_pool_bwd", s);
-  if (st != PACK3D_OK) return st;
+  if (!reuse_forward) {
+    // recompute the rotated and pooled operands into the forward part of the workspace
+    st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, "rope_pool_bwd", s);
+    if (st != PACK3D_OK) return st;
+  }
   return launch_attn_bwd(d, ix, at, coords, out, lse, dout, dq, dk, dv, (char*)ws, w, s);
 }

@@ -64,7 +64,7 @@ EXPORTS = {
     "pack3d_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 6
                        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pack3d_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 10
-                        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]),
     "pack3d_workspace_views": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn), ctypes.POINTER(Views)]),
     "pack3d_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
     "pack3d_profile_read": (ctypes.c_int32, [ctypes.c_char_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
@@ -217,8 +217,12 @@ def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, wit
 
 
 def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0, scale=None,
-             with_summaries=True, workspace: torch.Tensor | None = None):
-    """Gradients (dq, dk, dv) of sum(out * dout) with respect to the unrotated q, k, v."""
+             with_summaries=True, workspace: torch.Tensor | None = None, reuse_forward: bool = False):
+    """Gradients (dq, dk, dv) of sum(out * dout) with respect to the unrotated q, k, v.
+
+    reuse_forward=True: ``workspace`` is the one the forward of these inputs used (allocated
+    with workspace_bytes(..., for_backward=True)) and still holds its intermediates, so the
+    backward skips recomputing them."""
     lib = load_library()
     b, n, h, d = q.shape
     attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries)
@@ -228,12 +232,14 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
     if need == 0:
         raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
     if workspace is None:
+        if reuse_forward:
+            raise Pack3DError(E_INVALID, "reuse_forward needs the forward's workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     _check(lib.pack3d_backward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(coords.contiguous()), _ptr(out), _ptr(lse.contiguous()), _ptr(dout.contiguous()),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                               ctypes.c_void_p(_stream())))
+                               1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
     return dq, dk, dv
 
 
@@ -286,10 +292,18 @@ class Pack3DAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True):
-        out, lse = forward(index, q.contiguous(), k.contiguous(), v.contiguous(), coords, rope_base=rope_base,
-                           scale=scale, with_summaries=with_summaries)
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        # the workspace is sized for the backward and kept, so the backward reuses the
+        # forward's rotated and pooled operands instead of recomputing them
+        attn = make_attn(q.dtype, q.shape[2], q.shape[3], rope_base, scale, with_summaries)
+        need = workspace_bytes(index, attn, True)
+        if need == 0:
+            raise Pack3DError(E_UNSUPPORTED, load_library().pack3d_last_error().decode())
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        out, lse = forward(index, q, k, v, coords, rope_base=rope_base, scale=scale,
+                           with_summaries=with_summaries, workspace=ws)
         ctx.save_for_backward(q, k, v, out, lse)
-        ctx.index, ctx.coords = index, coords
+        ctx.index, ctx.coords, ctx.workspace = index, coords, ws
         ctx.opts = (rope_base, scale, with_summaries)
         return out
 
@@ -298,7 +312,9 @@ class Pack3DAttention(torch.autograd.Function):
         q, k, v, out, lse = ctx.saved_tensors
         rope_base, scale, with_summaries = ctx.opts
         dq, dk, dv = backward(ctx.index, q, k, v, ctx.coords, out, lse, dout.contiguous(), rope_base=rope_base,
-                              scale=scale, with_summaries=with_summaries)
+                              scale=scale, with_summaries=with_summaries, workspace=ctx.workspace,
+                              reuse_forward=True)
+        ctx.workspace = None
         return dq, dk, dv, None, None, None, None, None
 
 

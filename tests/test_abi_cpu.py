@@ -39,7 +39,7 @@ def test_exported_symbols_in_dynamic_table():
 
 def test_version_and_last_error():
     lib = p3.load_library()
-    assert lib.pack3d_version() == 100
+    assert lib.pack3d_version() == 101
     assert isinstance(lib.pack3d_last_error(), bytes)
 
 
@@ -90,5 +90,5 @@ def test_forward_argument_errors_return_codes():
     st = lib.pack3d_forward(None, ctypes.byref(at), *([None] * 6), None, 0, None)
     assert st == p3.E_INVALID
     assert lib.pack3d_workspace_bytes(None, ctypes.byref(at), 0) == 0
-    st = lib.pack3d_backward(None, ctypes.byref(at), *([None] * 10), None, 0, None)
+    st = lib.pack3d_backward(None, ctypes.byref(at), *([None] * 10), None, 0, 0, None)
     assert st == p3.E_INVALID

@@ -114,3 +114,23 @@ def test_backward_poisoned_workspace():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_reusing_forward_workspace_bitwise(dtype):
+    """reuse_forward skips recomputing the forward's intermediates; gradients are bitwise equal."""
+    w = si.small_workload(grid=(8, 8, 16), block=(4, 4, 4), heads=2, head_dim=96, packing="random", seed=21)
+    say(f"backward reuse {dtype}")
+    xd = to_dev(si.make_inputs(w, dtype, with_grad=True))
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    attn = p3.make_attn(dtype, w.heads, w.head_dim)
+    ws = torch.full((p3.workspace_bytes(ix, attn, True),), 255, dtype=torch.uint8, device=DEV)
+    out, lse = p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], workspace=ws)
+    ref = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"])
+    got = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws,
+                      reuse_forward=True)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+    with pytest.raises(p3.Pack3DError):
+        p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], reuse_forward=True)
