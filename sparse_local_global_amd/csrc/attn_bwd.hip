@@ -407,6 +407,88 @@ struct LocSmem32 {
   int src[kTile], rel[kTile * 3];
 };
 
+// Epilogue of bwd_local32 for D = 96, in registers.  Each RoPE axis is then exactly
+// one 32-dim accumulator block (dt = axis) and the pair (k, k + 16) of a rotation sits in
+// slots i and i + 8 of the same lane, so R^T needs no data exchange.  The two query
+// halves swap partial sums through LDS (half 1 sends dK~, half 0 sends dV); half 0 then
+// finishes dk = R^T (scale * acc + dKbar / |b|), half 1 dv = acc + dVbar / |b|, and each
+// lane stores its key's 48 values as 8-byte pieces.
+__device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32x16 (&dv)[3], f32x4* part, int b,
+                                          int h, int kb, int krow0, int kloc, int nk, int qh, int lane, int half) {
+  constexpr int NDT = 3;
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        part[(4 * dt + q) * 64 + lane] = f32x4{dk[dt][4 * q], dk[dt][4 * q + 1], dk[dt][4 * q + 2], dk[dt][4 * q + 3]};
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        part[(4 * NDT + 4 * dt + q) * 64 + lane] =
+            f32x4{dv[dt][4 * q], dv[dt][4 * q + 1], dv[dt][4 * q + 2], dv[dt][4 * q + 3]};
+  }
+  __syncthreads();
+  const int64_t bh = (int64_t)b * a.H + h;
+  const float inv = 1.0f / (float)a.bvol;
+  f32x16(&acc)[NDT] = dk;  // the half's own tensor; filled below for qh = 1
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = dv[dt];
+  }
+  const int pslot = qh == 0 ? 0 : 4 * NDT;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 pv = part[(pslot + 4 * dt + q) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[dt][4 * q + e] += pv[e];
+    }
+  if (kloc >= nk) return;
+  const float* sb = (qh == 0 ? a.dkbar : a.dvbar) + (bh * a.nblkp + kb) * 96;
+  const float mul = qh == 0 ? a.scale : 1.0f;
+  // value of dim 32dt + 8jj + 4half + e is slot 4jj + e of block dt
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 sv = a.with_summaries ? *(const f32x4*)(sb + 32 * dt + 8 * jj + 4 * half) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[dt][4 * jj + e] = acc[dt][4 * jj + e] * mul + sv[e] * inv;
+    }
+  const int row = krow0 + kloc;
+  const int src = a.perm[(int64_t)b * a.N + row];
+  if (qh == 0) {
+    const int32_t* g = a.geom + b * G_FIELDS;
+    const int32_t* c = a.coords + ((int64_t)b * a.N + src) * 3;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      int r = c[dt] - g[G_OZ + dt];
+      r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);
+      const float2* cs = a.tab + (int64_t)r * 16 + 4 * half;  // half = 16 pairs per axis
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 t = cs[8 * j + e];
+          const float lo = acc[dt][4 * j + e], hi = acc[dt][4 * j + 8 + e];
+          acc[dt][4 * j + e] = lo * t.x + hi * t.y;       // y1 c + y2 s
+          acc[dt][4 * j + 8 + e] = -lo * t.y + hi * t.x;  // -y1 s + y2 c
+        }
+    }
+  }
+  bf16* dst = (bf16*)(qh == 0 ? a.dk : a.dv) + (((int64_t)b * a.N + src) * a.H + h) * 96;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *(bf16x4*)(dst + 32 * dt + 8 * jj + 4 * half) =
+          bf16x4{(bf16)acc[dt][4 * jj], (bf16)acc[dt][4 * jj + 1], (bf16)acc[dt][4 * jj + 2], (bf16)acc[dt][4 * jj + 3]};
+}
+
 // Direct copy of lse2 / delta for tile rows 16 w .. 16 w + 15 (lanes 0..15 of wave w).
 __device__ inline void issue_rows16(const Src& src, float* dst16, uint32_t byte_off) {
   if ((threadIdx.x & 63) < 16)
@@ -501,6 +583,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __syncthreads();  // the partial and staging buffers overlay the stages
 
   constexpr int NDT = DP / 32;
+  if constexpr (DP == 96) {
+    if (a.D == 96) {
+      local32_epilogue96(a, dk, dv, (f32x4*)(kh == 0 ? (void*)&s0 : (void*)&s1), b, h, kb, krow0, kloc, nk,
+                         qh, lane, half);
+      return;
+    }
+  }
   f32x4* part = (f32x4*)(kh == 0 ? (void*)&s0 : (void*)&s1);  // [slot][lane]
   float(*st)[DP + 1] = (float(*)[DP + 1]) & s2;
   if (qh == 1) {

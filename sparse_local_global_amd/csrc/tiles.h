@@ -148,28 +148,31 @@ typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
 // Transpose read: lane j of a 16-lane group points at row r0 + j/4, columns
 // c0 + 4(j%4) .. +3 (c0 a multiple of 16), and receives rows r0 .. r0+3 of column c0 + j.
-// column_bases() gives the lane's pointers for r0 & 15 = r15 and c0 an even / odd
-// multiple of 16; G::off(r0 & ~15, 4 * (c0 / 32)) completes the address.
+// column_bases() gives the lane's element offsets for r0 & 15 = r15 and c0 an even /
+// odd multiple of 16; G::off(r0 & ~15, 4 * (c0 / 32)) completes the address.
 struct ColumnBases {
-  const bf16* even;  // c0 = 32n
-  const bf16* odd;   // c0 = 32n + 16
+  int even;  // element offset in the tile for c0 = 32n
+  int odd;   // for c0 = 32n + 16
 };
 template <int DP>
-__device__ inline ColumnBases column_bases(const RowTile<bf16, DP>& t, int r15, int lane16) {
+__device__ inline ColumnBases column_bases(int r15, int lane16) {
   using G = TileGeom<bf16, DP>;
   const int r = r15 + (lane16 >> 2);  // r15: a multiple of 4 below 16
   const int c = 4 * (lane16 & 3);     // column of this lane's piece within c0 .. c0+15
-  return {t.x + G::base(r, c >> 3) + (c & 7), t.x + G::base(r, 2 + (c >> 3)) + (c & 7)};
+  return {G::base(r, c >> 3) + (c & 7), G::base(r, 2 + (c >> 3)) + (c & 7)};
 }
-__device__ inline bf16x4 read_tr(const bf16* p) {
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_bf16*)p);
+// Element offsets (not pointers) select the lane's base, so every LDS address stays a
+// plain offset from the tile object.
+template <int DP>
+__device__ inline bf16x4 read_tr(const RowTile<bf16, DP>& t, int off) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_bf16*)(t.x + off));
   return __builtin_bit_cast(bf16x4, v);
 }
 
 template <int DP>
 __device__ inline void accum(const RowTile<bf16, DP>& t, const f32x4 (&p)[4], f32x4 (&acc)[DP / 16], int col, int grp) {
   using G = TileGeom<bf16, DP>;
-  const ColumnBases cb = column_bases(t, 4 * grp, col);  // rows 32c (+16) + 4grp + col/4
+  const ColumnBases cb = column_bases<DP>(4 * grp, col);  // rows 32c (+16) + 4grp + col/4
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     bf16x8 b;
@@ -180,9 +183,9 @@ __device__ inline void accum(const RowTile<bf16, DP>& t, const f32x4 (&p)[4], f3
     }
 #pragma unroll
     for (int dt = 0; dt < DP / 16; ++dt) {
-      const bf16* cp = dt & 1 ? cb.odd : cb.even;  // columns 16dt ..
-      const bf16x4 lo = read_tr(cp + G::off(32 * c, 4 * (dt >> 1)));
-      const bf16x4 hi = read_tr(cp + G::off(32 * c + 16, 4 * (dt >> 1)));
+      const int cp = dt & 1 ? cb.odd : cb.even;  // columns 16dt ..
+      const bf16x4 lo = read_tr(t, cp + G::off(32 * c, 4 * (dt >> 1)));
+      const bf16x4 hi = read_tr(t, cp + G::off(32 * c + 16, 4 * (dt >> 1)));
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[dt], 0, 0, 0);
     }
@@ -249,9 +252,9 @@ __device__ inline void accum32(const RowTile<bf16, DP>& t, const f32x16 (&p)[2],
   using G = TileGeom<bf16, DP>;
   const int lane16 = lane & 15, hi16 = (lane >> 4) & 1;
   // rows 16s + 4h (+8) + lane16/4, columns 32dt + 16hi16 + lane16
-  const ColumnBases c0 = column_bases(t, 4 * half, lane16), c8 = column_bases(t, 8 + 4 * half, lane16);
-  const bf16* p0 = hi16 ? c0.odd : c0.even;
-  const bf16* p8 = hi16 ? c8.odd : c8.even;
+  const ColumnBases c0 = column_bases<DP>(4 * half, lane16), c8 = column_bases<DP>(8 + 4 * half, lane16);
+  const int p0 = hi16 ? c0.odd : c0.even;
+  const int p8 = hi16 ? c8.odd : c8.even;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     // rows 16s + 4h + e (e < 4) and 16s + 8 + 4h + (e - 4): accumulator slots 8(s%2) + e
@@ -262,8 +265,8 @@ __device__ inline void accum32(const RowTile<bf16, DP>& t, const f32x16 (&p)[2],
     for (int e = 0; e < 8; ++e) b[e] = (bf16)ps[i0 + e];
 #pragma unroll
     for (int dt = 0; dt < DP / 32; ++dt) {
-      const bf16x4 lo = read_tr(p0 + G::off(16 * s, 4 * dt));
-      const bf16x4 hi = read_tr(p8 + G::off(16 * s, 4 * dt));
+      const bf16x4 lo = read_tr(t, p0 + G::off(16 * s, 4 * dt));
+      const bf16x4 hi = read_tr(t, p8 + G::off(16 * s, 4 * dt));
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
     }
@@ -299,9 +302,9 @@ __device__ inline void accum32_rows(const RowTile<bf16, DP>& t, const f32x16& p,
                                     int half, int mt) {
   using G = TileGeom<bf16, DP>;
   const int lane16 = lane & 15, hi16 = (lane >> 4) & 1;
-  const ColumnBases c0 = column_bases(t, 4 * half, lane16), c8 = column_bases(t, 8 + 4 * half, lane16);
-  const bf16* p0 = hi16 ? c0.odd : c0.even;
-  const bf16* p8 = hi16 ? c8.odd : c8.even;
+  const ColumnBases c0 = column_bases<DP>(4 * half, lane16), c8 = column_bases<DP>(8 + 4 * half, lane16);
+  const int p0 = hi16 ? c0.odd : c0.even;
+  const int p8 = hi16 ? c8.odd : c8.even;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     // rows 32mt + 16s + 4h + e (e < 4) and 32mt + 16s + 8 + 4h + (e - 4): slots 8s + e
@@ -310,8 +313,8 @@ __device__ inline void accum32_rows(const RowTile<bf16, DP>& t, const f32x16& p,
     for (int e = 0; e < 8; ++e) b[e] = (bf16)p[8 * s + e];
 #pragma unroll
     for (int dt = 0; dt < DP / 32; ++dt) {
-      const bf16x4 lo = read_tr(p0 + G::off(32 * mt + 16 * s, 4 * dt));
-      const bf16x4 hi = read_tr(p8 + G::off(32 * mt + 16 * s, 4 * dt));
+      const bf16x4 lo = read_tr(t, p0 + G::off(32 * mt + 16 * s, 4 * dt));
+      const bf16x4 hi = read_tr(t, p8 + G::off(32 * mt + 16 * s, 4 * dt));
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
     }

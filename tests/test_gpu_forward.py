@@ -65,6 +65,7 @@ CASES = [
     ((8, 8, 8), (2, 2, 4), 2, 2, 120, "random", 1, torch.bfloat16),  # Dp 128, r = 2
     ((8, 8, 8), (4, 4, 4), 0, 1, 66, "random", 1, torch.float32),    # r = 0, Dp 96 with padding
     ((4, 8, 8), (2, 2, 2), 3, 2, 24, "raster", 1, torch.bfloat16),   # r = 3 (slots 343)
+    ((8, 8, 8), (2, 2, 4), 1, 2, 90, "morton", 1, torch.bfloat16),   # Dp 96 with padding, bvol 16
 ]
 
 
