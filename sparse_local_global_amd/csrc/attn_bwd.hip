@@ -691,6 +691,34 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
   accum(sm.u.t.k, dp, dq, col, grp);
 }
 
+// Epilogue of bwd_dq for D = 96, in registers: lane (query, group g) holds dims
+// 16dt + 4g + i, so the rotation pair (k, k + 16) of axis ax is blocks 2ax and 2ax + 1 of
+// the same lane; dq = R^T (scale * acc) is stored as 4-element pieces.
+template <typename T>
+__device__ inline void dq_epilogue96(const BwdArgs& a, f32x4 (&dq)[6], int b, int h, int row, bool ok, int grp) {
+  if (!ok) return;
+  const int src = a.perm[(int64_t)b * a.N + row];
+  const int32_t* g = a.geom + b * G_FIELDS;
+  const int32_t* c = a.coords + ((int64_t)b * a.N + src) * 3;
+  T* dst = (T*)a.dq + (((int64_t)b * a.N + src) * a.H + h) * 96;
+#pragma unroll
+  for (int ax = 0; ax < 3; ++ax) {
+    int r = c[ax] - g[G_OZ + ax];
+    r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);
+    const float2* cs = a.tab + (int64_t)r * 16 + 4 * grp;  // 16 pairs per axis
+    Vec<T, 4> lo4, hi4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2 t = cs[i];
+      const float lo = dq[2 * ax][i] * a.scale, hi = dq[2 * ax + 1][i] * a.scale;
+      lo4.v[i] = (T)(lo * t.x + hi * t.y);   // y1 c + y2 s
+      hi4.v[i] = (T)(-lo * t.y + hi * t.x);  // -y1 s + y2 c
+    }
+    *(Vec<T, 4>*)(dst + 32 * ax + 4 * grp) = lo4;
+    *(Vec<T, 4>*)(dst + 32 * ax + 16 + 4 * grp) = hi4;
+  }
+}
+
 template <typename T, int DP, bool ONE_BLOCK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dq(BwdArgs a) {
   __shared__ DqSmem<T, DP> sm;
@@ -771,6 +799,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     dq_step(sm, qf, gf, dq, lse2, delta, c, col, grp, live);
   };
   pipeline2(total, st0, st1, fetch, store, compute);
+  if constexpr (DP == 96) {
+    if (a.D == 96) {
+      dq_epilogue96<T>(a, dq, b, h, qrow0 + qloc, qok, grp);
+      return;
+    }
+  }
   __syncthreads();  // the staging area below overlays the tiles
 #pragma unroll
   for (int dt = 0; dt < DP / 16; ++dt) {

@@ -363,12 +363,23 @@ __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2)))
     const int src = a.perm[(int64_t)b * N + qrow0 + qloc];
     const float inv = 1.0f / l;
     bf16* orow = (bf16*)a.out + (((int64_t)b * N + src) * a.H + h) * a.D;
+    if (a.D == DP) {
+      // slots 4j .. 4j+3 are consecutive dims: 8-byte stores
 #pragma unroll
-    for (int dt = 0; dt < DP / 32; ++dt) {
+      for (int dt = 0; dt < DP / 32; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (d < a.D) orow[d] = (bf16)(st.o[dt][i] * inv);
+        for (int j = 0; j < 4; ++j)
+          *(bf16x4*)(orow + 32 * dt + 8 * j + 4 * half) =
+              bf16x4{(bf16)(st.o[dt][4 * j] * inv), (bf16)(st.o[dt][4 * j + 1] * inv),
+                     (bf16)(st.o[dt][4 * j + 2] * inv), (bf16)(st.o[dt][4 * j + 3] * inv)};
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int d = 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (d < a.D) orow[d] = (bf16)(st.o[dt][i] * inv);
+        }
       }
     }
     if (half == 0) a.lse[bh * N + src] = st.m * kLn2 + logf(l);
