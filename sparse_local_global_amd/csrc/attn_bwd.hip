@@ -719,8 +719,10 @@ __device__ inline void dq_epilogue96(const BwdArgs& a, f32x4 (&dq)[6], int b, in
   }
 }
 
+// three waves per SIMD where the registers allow it (a wider head dim would spill)
 template <typename T, int DP, bool ONE_BLOCK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DP * sizeof(T) <= 192 ? 3 : 2)))
+void k_bwd_dq(BwdArgs a) {
   __shared__ DqSmem<T, DP> sm;
   const int ntile = a.nblk * a.tiles_per_block;
   const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
@@ -815,129 +817,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   write_rows<T>(a, &sm.u.st[0][0], DP + 1, nq, b, h, qrow0, true, (T*)a.dq, sm.src, sm.rel);
 }
 
-// ---------------------------------------------------------------------------------
-// bwd_dq for bf16 with 32 query columns per wave (two waves per 64-query tile):
-// v_mfma_f32_32x32x16_bf16 halves the LDS reads per multiply, as in the forward.
-// ---------------------------------------------------------------------------------
-constexpr int kThreads32 = 128;
-
-template <int DP>
-struct DqSmem32 {
-  union {
-    struct {
-      RowTile<bf16, DP> k, v;
-    } t;
-    float st[kTile][DP + 1];
-  } u;
-  int list[kMaxSlots];
-  uint32_t mask[kMaxBlocks / 32];
-  int nloc;
-  int src[kTile], rel[kTile * 3];
-};
-
-template <int DP, bool ONE_BLOCK>
-__global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_dq32(BwdArgs a) {
-  __shared__ DqSmem32<DP> sm;
-  const int ntile = a.nblk * a.tiles_per_block;
-  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
-  const int qb = tile / a.tiles_per_block, qs = tile - qb * a.tiles_per_block;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 31, half = lane >> 5;
-  const int N = a.N, bvol = a.bvol;
-  const int64_t bh = (int64_t)b * a.H + h;
-  const int nq = bvol < kTile ? bvol : kTile;
-  const int qrow0 = qb * bvol + qs * kTile;
-  const int qloc = 32 * wave + col;
-  const bool qok = qloc < nq;
-  ColFrag32<DP> qf, gf;
-  qf.load((const bf16*)a.qrot + (bh * N + qrow0 + qloc) * DP, qok, half);
-  gf.load((const bf16*)a.doc + (bh * N + qrow0 + qloc) * DP, qok, half);
-  const float lse2 = qok ? a.lsec[bh * N + qrow0 + qloc] : INFINITY;
-  const float delta = qok ? a.delta[bh * N + qrow0 + qloc] : 0.f;
-
-  const int mask_words = a.nblkp / 32;
-  for (int i = tid; i < mask_words; i += kThreads32) sm.mask[i] = 0u;
-  if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
-  __syncthreads();
-  const int nloc = sm.nloc;
-  for (int i = tid; i < nloc; i += kThreads32) atomicOr(&sm.mask[sm.list[i] >> 5], 1u << (sm.list[i] & 31));
-  f32x16 dq[DP / 32];
-#pragma unroll
-  for (int dt = 0; dt < DP / 32; ++dt) dq[dt] = f32x16{};
-
-  const size_t slice = (size_t)N * DP * sizeof(bf16), sslice = (size_t)a.nblkp * DP * sizeof(bf16);
-  const Src krot((const bf16*)a.krot + bh * N * DP, slice);
-  const Src vrow((const bf16*)a.vr + bh * N * DP, slice);
-  const Src kbar((const bf16*)a.kbar + bh * a.nblkp * DP, sslice);
-  const Src vbar((const bf16*)a.vbar + bh * a.nblkp * DP, sslice);
-  const float c = a.scale_log2;
-  const int nkeys = nloc * bvol;
-  const int nlt = (nkeys + kTile - 1) / kTile;
-  const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
-  struct Stage {
-    RowRegs<bf16, DP, kThreads32> k, v;
-  } st0;
-  auto fetch = [&](Stage& S, int t) {
-    if (t < nlt) {
-      const int j0 = t * kTile;
-      const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
-      const VirtualRows vr(sm.list, bvol, j0);
-      if constexpr (ONE_BLOCK) {
-        const int row0 = vr.blk0 * bvol + vr.off0;
-        S.k.fetch_at(krot, (uint32_t)row0 * DP);
-        S.v.fetch_at(vrow, (uint32_t)row0 * DP);
-      } else {
-        S.k.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
-        S.v.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
-      }
-    } else {
-      const int r0 = (t - nlt) * kTile;
-      S.k.fetch_at(kbar, (uint32_t)r0 * DP);
-      S.v.fetch_at(vbar, (uint32_t)r0 * DP);
-    }
-  };
-  auto store = [&](const Stage& S) {
-    S.k.store(sm.u.t.k);
-    S.v.store(sm.u.t.v);
-  };
-  auto compute = [&](int t) {
-    uint64_t live;
-    if (t < nlt) {
-      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
-      live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
-    } else {
-      const int ts = t - nlt, r0 = ts * kTile;
-      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
-      const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
-      live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
-    }
-    f32x16 sc[2], dp[2];
-    score32(sm.u.t.k, qf, sc, col, half);
-    score32(sm.u.t.v, gf, dp, col, half);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 32 * mt + 8 * (i >> 2) + 4 * half + (i & 3);
-        float p = fast_exp2(fmaf(sc[mt][i], c, -lse2));
-        if (live != ~0ull && !((live >> r) & 1ull)) p = 0.f;
-        dp[mt][i] = p * (dp[mt][i] - delta);
-      }
-    }
-    accum32(sm.u.t.k, dp, dq, lane, half);
-  };
-  pipeline1(total, st0, fetch, store, compute);
-  __syncthreads();  // the staging area below overlays the tiles
-#pragma unroll
-  for (int dt = 0; dt < DP / 32; ++dt) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.u.st[qloc][32 * dt + 8 * (i >> 2) + 4 * half + (i & 3)] = dq[dt][i] * a.scale;
-  }
-  __syncthreads();
-  write_rows<bf16>(a, &sm.u.st[0][0], DP + 1, nq, b, h, qrow0, true, (bf16*)a.dq, sm.src, sm.rel);
-}
-
 template <typename T, int DP, bool ONE_BLOCK>
 pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   const dim3 tiles(d.nblk * a.tiles_per_block * d.H * d.B);
@@ -962,11 +841,7 @@ pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   }
   {
     ProfileScope prof("bwd_dq", s);
-    // 32-column waves for bf16 only where their registers fit (Dp = 32)
-    if constexpr (sizeof(T) == 2 && DP <= 32)
-      hipLaunchKernelGGL((k_bwd_dq32<DP, ONE_BLOCK>), tiles, dim3(kThreads32), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_bwd_dq<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_dq<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
   }
   return check_launch("backward: attention");
 }
