@@ -141,7 +141,9 @@ __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, in
 }
 
 // ---------------------------------------------------------------------------------
-// bwd_summary: workgroup = (64 summaries, head, volume x query chunk)
+// bwd_summary: workgroup = (64 summaries, head, volume x query chunk).  Wide fp32 rows
+// (Dp >= 64) run one wave per SIMD so the accumulators can use the AGPRs instead of
+// spilling; bwd_local below does the same.
 // ---------------------------------------------------------------------------------
 template <typename T, int DP>
 struct SumSmem {
@@ -150,7 +152,8 @@ struct SumSmem {
 };
 
 template <typename T, int DP, bool ONE_BLOCK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_summary(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DP * sizeof(T) <= 192 ? 2 : 1, 2)))
+void k_bwd_summary(BwdArgs a) {
   __shared__ SumSmem<T, DP> sm;
   // 1-D grid over (summary tile, chunk, head, volume), summary tile fastest: the
   // workgroups that share a chunk's query tiles run on the same XCD
@@ -272,7 +275,8 @@ struct LocSmem {
 };
 
 template <typename T, int DP, bool ONE_BLOCK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_local(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DP * sizeof(T) <= 192 ? 2 : 1, 2)))
+void k_bwd_local(BwdArgs a) {
   __shared__ LocSmem<T, DP> sm;
   const int ntile = a.nblk * a.tiles_per_block;
   const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
