@@ -85,6 +85,20 @@ def time_region(fn, steps: int):
     return (time.perf_counter() - t0) * 1000.0 / steps
 
 
+def gemm_ceiling(steps: int = 20, n: int = 8192) -> dict:
+    """Attainable bf16 matrix-core rate on this GPU: a square torch.matmul (hipBLASLt), timed
+    after the step timings, as a reference beside the datasheet peak."""
+    import torch
+    a = torch.randn(n, n, device="cuda:0").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    ms = time_region(lambda: torch.matmul(a, b), steps)
+    del a, b
+    return {"tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12, "shape_mnk": [n, n, n], "ms": ms,
+            "library": "torch.matmul (hipBLASLt), bf16 in, fp32 accumulate"}
+
+
 def cpu_baseline(w, x, sample_blocks: int) -> dict:
     """The fp64 oracle on the host cores: all heads of the first `sample_blocks` query blocks of each volume."""
     import oracle  # test infrastructure, used only for this reported baseline
@@ -113,6 +127,7 @@ def main(argv=None) -> int:
     ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
     ap.add_argument("--cpu-sample-blocks", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-ceiling", action="store_true", help="skip the hipBLASLt GEMM reference")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args(argv)
@@ -264,6 +279,11 @@ def main(argv=None) -> int:
         "pairs_per_volume_head": {"local": local, "summary": summ},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if not args.no_gemm_ceiling:
+        g = gemm_ceiling()
+        result["gemm_ceiling"] = g
+        result["roofline"]["frac_of_gemm_ceiling"] = dk["tflops"] / g["tflops"]
+        result["attn_fwd_frac_of_gemm_ceiling"] = result["attn_fwd_tflops"] / g["tflops"]
     if not args.no_cpu_baseline:
         log(f"bench: timing the fp64 oracle on {args.cpu_sample_blocks} query blocks per volume")
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_blocks)

@@ -21,6 +21,9 @@ from .pack3d import (  # noqa: F401
     CoordsError,
     build_index,
     rope,
+    rope_1d,
+    rotate,
+    POSITION_MODES,
     rope_tables,
     pool_blocks,
     forward,

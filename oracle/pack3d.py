@@ -24,6 +24,14 @@ What is computed ("Geometry Matters in Packed 3D Attention", abstract):
 * Local logits and summary logits share one softmax (scale 1/sqrt(D) unless
   given).
 
+Position modes (controls).  The abstract contrasts axial RoPE on grid
+coordinates with position encodings indexed by the packed sequence, which
+break under repacking.  ``position_mode`` selects the angle source of the same
+operator: "axial" (the method), "packed1d" (standard RoPE on the packed
+sequence position: the rotation of the RoPE section applied to the whole head
+dim, pairs (k, k + D/2), theta_k = base^(-2k/D), angle = packed index * theta_k)
+and "none" (no rotation).  Locality and summaries always follow the grid.
+
 Readings where the pages are silent (each listed in the design notes):
 block lattice anchored at each volume's componentwise minimum coordinate; only
 full grids with extents divisible by the block are accepted; no causal mask;
@@ -152,6 +160,46 @@ def rope(x, coords, base: float = 10000.0, inverse: bool = False) -> np.ndarray:
     return out[:, 0, :] if squeeze else out
 
 
+def rope_1d(x, pos, base: float = 10000.0, inverse: bool = False) -> np.ndarray:
+    """Rotate x [N, H, D] (or [N, D]) by standard 1D RoPE at integer positions pos [N].
+
+    The whole head dim is one group: element k pairs with element k + D/2 and turns
+    by angle pos * theta_k with theta_k = base^(-2k/D) ("SpatioTemporal RoPE"
+    section: standard RoPE rotates by the 1D sequence position, half-split pairs).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    squeeze = x.ndim == 2
+    if squeeze:
+        x = x[:, None, :]
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("head_dim must be even")
+    half = d // 2
+    theta = rope_tables(d, base)
+    phi = np.asarray(pos, dtype=np.float64)[:, None] * theta[None, :]    # [N, half]
+    sign = -1.0 if inverse else 1.0
+    cos = np.cos(phi)[:, None, :]
+    sin = sign * np.sin(phi)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    out = np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+    return out[:, 0, :] if squeeze else out
+
+
+POSITION_MODES = ("axial", "packed1d", "none")
+
+
+def rotate(x, coords, packed_pos, base: float, mode: str, inverse: bool = False) -> np.ndarray:
+    """The rotation of ``mode``: axial RoPE on grid coordinates [N, 3], 1D RoPE on the
+    packed sequence positions [N], or none."""
+    if mode == "axial":
+        return rope(x, coords, base, inverse)
+    if mode == "packed1d":
+        return rope_1d(x, packed_pos, base, inverse)
+    if mode == "none":
+        return np.array(x, dtype=np.float64)
+    raise ValueError(f"unknown position mode {mode!r}")
+
+
 def pool_blocks(x_canon: np.ndarray, bvol: int) -> np.ndarray:
     """Mean over each block of a canonical-order array [N, ...] -> [nblk, ...]."""
     n = x_canon.shape[0]
@@ -176,7 +224,7 @@ def _f64(t) -> np.ndarray:
     return np.asarray(t, dtype=np.float64)
 
 
-def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None):
+def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None, position_mode="axial"):
     q, k, v = _f64(q), _f64(k), _f64(v)
     coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords)
     if coords.ndim == 2:
@@ -185,9 +233,9 @@ def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None):
     rc = coords if rope_coords is None else np.asarray(rope_coords)
     vols = []
     for vi, ix in enumerate(index):
-        perm = ix["perm"]
-        qt = rope(q[vi][perm], rc[vi][perm], base)
-        kt = rope(k[vi][perm], rc[vi][perm], base)
+        perm = ix["perm"]            # canonical slot -> packed position
+        qt = rotate(q[vi][perm], rc[vi][perm], perm, base, position_mode)
+        kt = rotate(k[vi][perm], rc[vi][perm], perm, base, position_mode)
         vc = v[vi][perm]
         vols.append(dict(ix=ix, qt=qt, kt=kt, vc=vc,
                          kbar=pool_blocks(kt, ix["bvol"]), vbar=pool_blocks(vc, ix["bvol"])))
@@ -209,16 +257,19 @@ def _key_rows(local, bvol):
 
 
 def forward(q, k, v, coords, block_shape, local_radius, *, rope_base=10000.0, scale=None,
-            with_summaries=True, query_blocks=None, rope_coords=None, return_logits=False):
+            with_summaries=True, query_blocks=None, rope_coords=None, return_logits=False,
+            position_mode="axial"):
     """PACK3D forward.  q, k, v [B, N, H, D]; coords [B, N, 3] (z, y, x).
 
     Returns (o [B, N, H, D], lse [B, H, N]) in fp64, packed order.  With
     ``query_blocks`` (a list of block ids) only those query blocks are
     computed in every volume; other rows are NaN.  ``return_logits`` (tiny
     inputs only) adds dense [B, H, N, N] local and [B, H, N, nblk] summary
-    logit matrices, NaN where a pair is not in the set.
+    logit matrices, NaN where a pair is not in the set.  ``position_mode`` picks the
+    rotation (see the module notes).
     """
-    q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base, rope_coords)
+    q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base, rope_coords,
+                                     position_mode)
     bsz, n, h, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = np.full((bsz, n, h, d), np.nan)
@@ -264,7 +315,7 @@ def forward(q, k, v, coords, block_shape, local_radius, *, rope_base=10000.0, sc
 
 
 def forward_naive(q, k, v, coords, block_shape, local_radius, *, rope_base=10000.0, scale=None,
-                  with_summaries=True):
+                  with_summaries=True, position_mode="axial"):
     """The definition token by token, with no index tables (tiny inputs only).
 
     Membership is decided by brute force: key j is local to query i when the
@@ -282,8 +333,9 @@ def forward_naive(q, k, v, coords, block_shape, local_radius, *, rope_base=10000
     for vi in range(bsz):
         c = coords[vi]
         bc = (c - c.min(axis=0)) // b                      # block coordinate of every token
-        qt = rope(q[vi], c, rope_base)
-        kt = rope(k[vi], c, rope_base)
+        pos = np.arange(n)                                 # tokens are in packed order here
+        qt = rotate(q[vi], c, pos, rope_base, position_mode)
+        kt = rotate(k[vi], c, pos, rope_base, position_mode)
         blocks = sorted({tuple(x) for x in bc.tolist()})
         members = {blk: np.nonzero((bc == np.asarray(blk)).all(axis=1))[0] for blk in blocks}
         kbar = {blk: kt[idx].mean(axis=0) for blk, idx in members.items()}
@@ -307,8 +359,9 @@ def forward_naive(q, k, v, coords, block_shape, local_radius, *, rope_base=10000
     return o, lse
 
 
-def dense_attention(q, k, v, coords, *, rope_base=10000.0, scale=None):
-    """Textbook softmax attention over every token of the volume, with 3D RoPE."""
+def dense_attention(q, k, v, coords, *, rope_base=10000.0, scale=None, position_mode="axial"):
+    """Textbook softmax attention over every token of the volume, with the rotation of
+    ``position_mode`` (3D RoPE by default)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords)
     bsz, n, h, d = q.shape
@@ -316,8 +369,9 @@ def dense_attention(q, k, v, coords, *, rope_base=10000.0, scale=None):
     o = np.empty_like(q)
     lse = np.empty((bsz, h, n))
     for vi in range(bsz):
-        qt = rope(q[vi], coords[vi], rope_base).transpose(1, 0, 2)
-        kt = rope(k[vi], coords[vi], rope_base).transpose(1, 0, 2)
+        pos = np.arange(n)
+        qt = rotate(q[vi], coords[vi], pos, rope_base, position_mode).transpose(1, 0, 2)
+        kt = rotate(k[vi], coords[vi], pos, rope_base, position_mode).transpose(1, 0, 2)
         s = scale * qt @ kt.transpose(0, 2, 1)
         m = s.max(-1, keepdims=True)
         e = np.exp(s - m)
@@ -331,7 +385,7 @@ def dense_attention(q, k, v, coords, *, rope_base=10000.0, scale=None):
 # --------------------------------------------------------------------------
 
 def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.0, scale=None,
-             with_summaries=True, volumes=None, heads=None):
+             with_summaries=True, volumes=None, heads=None, position_mode="axial"):
     """Gradients (dq, dk, dv) [B, N, H, D] fp64 of sum(o * do) w.r.t. unrotated q, k, v.
 
     With o_i = (sum_j P_ij V_j + sum_b P_ib Vbar_b), P = exp(logit - lse_i):
@@ -341,9 +395,11 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
       dK~_j = scale sum_i dS_ij Q~_i + dKbar_b(j) / |b|,  dKbar_b = scale sum_i dT_ib Q~_i
       dV_j  = sum_i P_ij dO_i + dVbar_b(j) / |b|,         dVbar_b = sum_i P_ib dO_i
       dq = R(c)^T dQ~, dk = R(c)^T dK~  (the mean pooling broadcasts 1/|b| to its members).
-    ``volumes`` / ``heads`` restrict the work (other entries are NaN).
+    ``volumes`` / ``heads`` restrict the work (other entries are NaN); R is the rotation of
+    ``position_mode``.
     """
-    q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base)
+    q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base,
+                                     position_mode=position_mode)
     do = _f64(do)
     bsz, n, h, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -404,8 +460,8 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
         dkt += unpool_grad(dkbar, bvol)
         dvc += unpool_grad(dvbar, bvol)
         c = coords[vi][perm]
-        dq_c = rope(dqt, c, rope_base, inverse=True)
-        dk_c = rope(dkt, c, rope_base, inverse=True)
+        dq_c = rotate(dqt, c, perm, rope_base, position_mode, inverse=True)
+        dk_c = rotate(dkt, c, perm, rope_base, position_mode, inverse=True)
         for src, dst in ((dq_c, dq), (dk_c, dk), (dvc, dv)):
             tmp = np.empty((n, len(hsel), d))
             tmp[perm] = src
