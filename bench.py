@@ -125,6 +125,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="65k")
     ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--position-mode", default="axial", choices=["axial", "packed1d", "none"],
+                    help="rotation of the timed step (axial grid-coordinate RoPE is the method)")
+    ap.add_argument("--no-mode-compare", action="store_true",
+                    help="skip timing the step under the other position modes")
     ap.add_argument("--cpu-sample-blocks", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true", help="skip the hipBLASLt GEMM reference")
@@ -161,30 +165,33 @@ def main(argv=None) -> int:
     t0 = time.perf_counter()
     ix = p3.build_index(xd["coords"], w.block, w.radius, order_hint=w.packing)
     index_ms = (time.perf_counter() - t0) * 1000.0
-    attn = p3.make_attn(dtype, w.heads, w.head_dim, w.rope_base)
-    ws = torch.empty(p3.workspace_bytes(ix, attn, True), dtype=torch.uint8, device="cuda:0")
+    mode = args.position_mode
+    ws_bytes = max(p3.workspace_bytes(ix, p3.make_attn(dtype, w.heads, w.head_dim, w.rope_base, position_mode=m),
+                                      True) for m in p3.POSITION_MODES)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
     out = torch.empty_like(xd["q"])
     lse = torch.empty((w.batch, w.heads, w.tokens), dtype=torch.float32, device="cuda:0")
 
     with_bwd = not args.forward_only
     if with_bwd:
         try:
-            p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws)
+            p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws,
+                        position_mode=mode)
         except p3.Pack3DError as e:
             if e.status != p3.E_UNSUPPORTED:
                 raise
             log(f"bench: backward not available ({e}); timing the forward only")
             with_bwd = False
 
-    def fwd(with_summaries=True):
+    def fwd(with_summaries=True, pm=None):
         p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], with_summaries=with_summaries,
-                   workspace=ws, out=out, lse=lse)
+                   workspace=ws, out=out, lse=lse, position_mode=pm or mode)
 
-    def step():
-        fwd()
+    def step(pm=None):
+        fwd(pm=pm)
         if with_bwd:
             p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws,
-                        reuse_forward=True)
+                        reuse_forward=True, position_mode=pm or mode)
 
     for _ in range(args.warmup):
         step()
@@ -209,6 +216,22 @@ def main(argv=None) -> int:
     prof_win = p3.profile_read()
     p3.profile_enable(False)
     log(f"bench: step {ms_step:.3f} ms, forward {ms_fwd:.3f} ms, windowed-only forward {ms_win:.3f} ms")
+
+    # the same step under the other rotations (controls of the operator): whole step and rope_pool
+    modes = {}
+    if not args.no_mode_compare:
+        for pm in p3.POSITION_MODES:
+            for _ in range(args.warmup):
+                step(pm)
+            ms = time_region(lambda: step(pm), args.steps)
+            p3.profile_reset()
+            p3.profile_enable(True)
+            time_region(lambda: step(pm), args.steps)
+            pp = p3.profile_read()
+            p3.profile_enable(False)
+            modes[pm] = {"ms_per_step": ms, "tokens_per_s": w.batch * w.tokens / (ms * 1e-3),
+                         "kernels_avg_ms": {k: t / max(n, 1) for k, (n, t) in pp.items()}}
+            log(f"bench: position mode {pm}: step {ms:.3f} ms")
 
     local, summ = pair_counts(ix.tables())
     bh = w.batch * w.heads
@@ -261,7 +284,8 @@ def main(argv=None) -> int:
         "config": {"workload": "65k", "pass": "forward+backward" if with_bwd else "forward",
                    "batch": w.batch, "grid_zyx": list(w.grid), "tokens_per_volume": w.tokens,
                    "tokens_per_step": tokens, "heads": w.heads, "head_dim": d, "block_zyx": list(w.block),
-                   "local_radius": w.radius, "packing": w.packing, "accumulation": "fp32"},
+                   "local_radius": w.radius, "packing": w.packing, "position_mode": mode,
+                   "accumulation": "fp32"},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": dk["frac"], "traffic": stored_traffic(dominant),
                      "flop_per_launch": dk["flop_per_launch"], "avg_launch_ms": dk["avg_ms"]},
@@ -279,6 +303,8 @@ def main(argv=None) -> int:
         "pairs_per_volume_head": {"local": local, "summary": summ},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if modes:
+        result["position_modes"] = modes
     if not args.no_gemm_ceiling:
         g = gemm_ceiling()
         result["gemm_ceiling"] = g

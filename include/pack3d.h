@@ -63,13 +63,30 @@ typedef struct pack3d_packing {
   int32_t order_hint; /* pack3d_order */
 } pack3d_packing;
 
+/* Angle source of the rotation ("Geometry Matters in Packed 3D Attention", abstract: the
+ * operator indexes every interaction with axial RoPE on grid coordinates rather than packed
+ * positions, and packed-position encodings break under repacking).  Locality and summaries
+ * always follow the grid; only the rotation of Q and K changes.
+ *   PACK3D_POS_AXIAL:     the method: head dim split into (z, y, x) groups of D/3, pairs
+ *                         (k, k + D/6), angle = grid coordinate * base^(-2k/(D/3)).
+ *   PACK3D_POS_PACKED_1D: control: standard 1D RoPE on the packed sequence position (the
+ *                         token's index in its volume), pairs (k, k + D/2), angle =
+ *                         position * base^(-2k/D) ("SpatioTemporal RoPE" section, 1D form).
+ *   PACK3D_POS_NONE:      control: no rotation. */
+typedef enum pack3d_position_mode {
+  PACK3D_POS_AXIAL = 0,
+  PACK3D_POS_PACKED_1D = 1,
+  PACK3D_POS_NONE = 2
+} pack3d_position_mode;
+
 /* Attention parameters.
  *   head_dim: D, split into three axis groups (z, y, x) of D/3 each; D % 6 == 0 and
  *             D <= 128 (inside each group element k pairs with element k + D/6).
  *   rope_base: base of the RoPE frequencies theta_k = base^(-2k/(D/3)) (e.g. 10000).
  *   softmax_scale: <= 0 selects 1/sqrt(D).
  *   with_summaries: 1 = PACK3D (local keys + distant block summaries),
- *                   0 = windowed-only (local keys only; the latency baseline). */
+ *                   0 = windowed-only (local keys only; the latency baseline).
+ *   position_mode:  pack3d_position_mode (0 = the method). */
 typedef struct pack3d_attn {
   int32_t dtype; /* pack3d_dtype */
   int32_t heads;
@@ -77,6 +94,7 @@ typedef struct pack3d_attn {
   float rope_base;
   float softmax_scale;
   int32_t with_summaries;
+  int32_t position_mode; /* pack3d_position_mode */
 } pack3d_attn;
 
 /* Opaque host handle describing one geometry (built once, reused by every call). */
@@ -173,9 +191,13 @@ pack3d_status pack3d_backward(const pack3d_index* index, const pack3d_attn* attn
 /* Where the forward leaves its intermediates inside the workspace (byte offsets),
  * for inspection by tests.  All arrays are in canonical order (block-major, raster
  * inside each block), elements of attn->dtype except rope_table (float2 cos, sin).
+ *   rope_table [extent_table, P]     cos and sin of angle row r, pair k; P = D/6 pairs per
+ *                                    axis group (axial), D/2 (packed 1D) or D/2 with the
+ *                                    single row 0 (no rotation)
  *   qrot, krot, vrow [B, H, N, Dp]   rotated Q and K, and V, rows zero-padded to Dp
  *   kbar, vbar [B, H, nblk_pad, Dp]  block means of the rotated K and of V (zero padding rows)
- * Rotation angles use coordinates relative to each volume's origin. */
+ * Axial rotation angles use coordinates relative to each volume's origin (rows =
+ * extents); packed 1D angles use the packed position (rows = N). */
 typedef struct pack3d_views {
   size_t rope_table, qrot, krot, vrow, kbar, vbar;
   int32_t head_dim_padded, nblk_padded, extent_table;

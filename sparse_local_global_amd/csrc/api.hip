@@ -34,6 +34,9 @@ pack3d_status check_attn(const pack3d_index* ix, const pack3d_attn* at, const ch
   if (at->heads < 1) return set_error(PACK3D_E_INVALID, "%s: heads must be >= 1", who);
   if (at->head_dim < 6 || at->head_dim % 6 || at->head_dim > 128)
     return set_error(PACK3D_E_UNSUPPORTED, "%s: head_dim %d must be a multiple of 6 in [6, 128]", who, at->head_dim);
+  if (at->position_mode != PACK3D_POS_AXIAL && at->position_mode != PACK3D_POS_PACKED_1D &&
+      at->position_mode != PACK3D_POS_NONE)
+    return set_error(PACK3D_E_INVALID, "%s: position_mode %d is not one of 0, 1, 2", who, at->position_mode);
   if (!(at->rope_base > 0.0f) || !std::isfinite(at->rope_base))
     return set_error(PACK3D_E_INVALID, "%s: rope_base must be positive and finite", who);
   if (!std::isfinite(at->softmax_scale))
@@ -57,7 +60,7 @@ using namespace pack3d;
 
 extern "C" const char* pack3d_last_error(void) { return g_msg; }
 
-extern "C" int32_t pack3d_version(void) { return 101; }
+extern "C" int32_t pack3d_version(void) { return 102; }
 
 extern "C" size_t pack3d_workspace_bytes(const pack3d_index* ix, const pack3d_attn* at, int for_backward) {
   if (check_attn(ix, at, "workspace_bytes") != PACK3D_OK) return 0;
@@ -73,7 +76,7 @@ extern "C" pack3d_status pack3d_workspace_views(const pack3d_index* ix, const pa
   Workspace w = workspace_layout(d);
   out->rope_table = w.rope; out->qrot = w.qrot; out->krot = w.krot; out->vrow = w.vr;
   out->kbar = w.kbar; out->vbar = w.vbar;
-  out->head_dim_padded = d.Dp; out->nblk_padded = d.nblkp; out->extent_table = d.emax;
+  out->head_dim_padded = d.Dp; out->nblk_padded = d.nblkp; out->extent_table = d.trows;
   return PACK3D_OK;
 }
 

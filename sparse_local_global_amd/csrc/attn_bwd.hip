@@ -42,7 +42,8 @@ struct BwdArgs {
   const void* out; const float* lse; const void* dout;
   void* dq; void* dk; void* dv;
   const int32_t* coords; const int32_t* perm; const int32_t* nbr; const int32_t* geom;
-  int B, N, H, D, Dp, nblk, nblkp, bvol, slots, radius, tiles_per_block, with_summaries, chunks, half, emax;
+  int B, N, H, D, Dp, nblk, nblkp, bvol, slots, radius, tiles_per_block, with_summaries, chunks;
+  int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
   int bz, by, bx;
   float scale, scale_log2;
 };
@@ -117,19 +118,16 @@ __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, in
     s_src[tid] = src;
     const int32_t* g = a.geom + b * G_FIELDS;
     const int32_t* c = a.coords + ((int64_t)b * N + src) * 3;
-    for (int ax = 0; ax < 3; ++ax) {
-      int r = c[ax] - g[G_OZ + ax];
-      r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);
-      s_rel[tid * 3 + ax] = r;
-    }
+    for (int gi = 0; gi < a.groups; ++gi) s_rel[tid * 3 + gi] = rope_row(a.pos_mode, gi, src, c, g, a.trows);
   }
   __syncthreads();
-  const int da = D / 3, half = a.half;
+  const int gw = a.gw, half = a.half;
+  unrotate = unrotate && a.pos_mode != PACK3D_POS_NONE;
   for (int it = tid; it < nrows * D; it += (int)blockDim.x) {
     const int r = it / D, col = it - r * D;
     float v = st[r * sts + col];
     if (unrotate) {
-      const int ax = col / da, k = col - ax * da;
+      const int ax = col / gw, k = col - ax * gw;
       const int kk = k < half ? k : k - half;
       const float2 cs = a.tab[(int64_t)s_rel[r * 3 + ax] * half + kk];
       if (k < half) v = v * cs.x + st[r * sts + col + half] * cs.y;      // y1 c + y2 s
@@ -471,7 +469,7 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       int r = c[dt] - g[G_OZ + dt];
-      r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);
+      r = r < 0 ? 0 : (r >= a.trows ? a.trows - 1 : r);
       const float2* cs = a.tab + (int64_t)r * 16 + 4 * half;  // half = 16 pairs per axis
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -588,7 +586,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   constexpr int NDT = DP / 32;
   if constexpr (DP == 96) {
-    if (a.D == 96) {
+    if (a.D == 96 && a.pos_mode == PACK3D_POS_AXIAL) {
       local32_epilogue96(a, dk, dv, (f32x4*)(kh == 0 ? (void*)&s0 : (void*)&s1), b, h, kb, krow0, kloc, nk,
                          qh, lane, half);
       return;
@@ -708,7 +706,7 @@ __device__ inline void dq_epilogue96(const BwdArgs& a, f32x4 (&dq)[6], int b, in
 #pragma unroll
   for (int ax = 0; ax < 3; ++ax) {
     int r = c[ax] - g[G_OZ + ax];
-    r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);
+    r = r < 0 ? 0 : (r >= a.trows ? a.trows - 1 : r);
     const float2* cs = a.tab + (int64_t)r * 16 + 4 * grp;  // 16 pairs per axis
     Vec<T, 4> lo4, hi4;
 #pragma unroll
@@ -806,7 +804,7 @@ void k_bwd_dq(BwdArgs a) {
   };
   pipeline2(total, st0, st1, fetch, store, compute);
   if constexpr (DP == 96) {
-    if (a.D == 96) {
+    if (a.D == 96 && a.pos_mode == PACK3D_POS_AXIAL) {
       dq_epilogue96<T>(a, dq, b, h, qrow0 + qloc, qok, grp);
       return;
     }
@@ -903,7 +901,7 @@ pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3
   a.tiles_per_block = d.bvol > kTile ? d.bvol / kTile : 1;
   a.with_summaries = at->with_summaries ? 1 : 0;
   a.chunks = summary_chunks(d);
-  a.half = d.half; a.emax = d.emax;
+  a.pos_mode = d.pos_mode; a.groups = d.groups; a.gw = d.gw; a.half = d.half; a.trows = d.trows;
   a.bz = ix->block[0]; a.by = ix->block[1]; a.bx = ix->block[2];
   a.scale = at->softmax_scale > 0.f ? at->softmax_scale : 1.0f / std::sqrt((float)d.D);
   a.scale_log2 = a.scale * kLog2e;

@@ -13,7 +13,10 @@ constexpr int kTile = 64;             // query rows / key rows per tile
 inline int padded_head_dim(int d) { return (d + 31) / 32 * 32; }
 
 struct Dims {
-  int B, N, H, D, Dp, nblk, nblkp, bvol, slots, emax, half;
+  int B, N, H, D, Dp, nblk, nblkp, bvol, slots, emax;
+  // rotation: `groups` contiguous head-dim groups of width gw, `half` = gw / 2 pairs
+  // (k, k + half) each, table of `trows` angle rows (positions) x half
+  int pos_mode, groups, gw, half, trows;
   size_t esize;  // bytes per element of the activation dtype
 };
 
@@ -26,7 +29,11 @@ inline Dims make_dims(const pack3d_index* ix, const pack3d_attn* at) {
   d.emax = ix->extent_max[0];
   if (ix->extent_max[1] > d.emax) d.emax = ix->extent_max[1];
   if (ix->extent_max[2] > d.emax) d.emax = ix->extent_max[2];
-  d.half = at->head_dim / 6;
+  d.pos_mode = at->position_mode;
+  d.groups = d.pos_mode == PACK3D_POS_AXIAL ? 3 : 1;
+  d.gw = d.D / d.groups;
+  d.half = d.gw / 2;
+  d.trows = d.pos_mode == PACK3D_POS_AXIAL ? d.emax : (d.pos_mode == PACK3D_POS_PACKED_1D ? d.N : 1);
   d.esize = at->dtype == PACK3D_BF16 ? 2 : 4;
   return d;
 }
@@ -55,7 +62,7 @@ inline Workspace workspace_layout(const Dims& d) {
   const size_t summ32 = bh * d.nblkp * d.Dp * sizeof(float);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-  w.rope = take(sizeof(float) * 2 * (size_t)d.emax * d.half);
+  w.rope = take(sizeof(float) * 2 * (size_t)d.trows * d.half);
   w.qrot = take(act);
   w.krot = take(act);
   w.vr = take(act);
@@ -71,6 +78,19 @@ inline Workspace workspace_layout(const Dims& d) {
   w.part_v = take(summ32 * summary_chunks(d));
   w.bwd_total = off;
   return w;
+}
+
+// Row of the rotation table for group g of the token at packed position src (its
+// coordinates at coords[0..2]): axial mode: the origin-relative coordinate on axis g,
+// clamped to the table (in range whenever the coordinates match the index); packed 1D:
+// the packed position; no rotation: row 0, whose angle is 0.
+__device__ inline int rope_row(int mode, int g, int src, const int32_t* coords, const int32_t* geom, int trows) {
+  if (mode == PACK3D_POS_AXIAL) {
+    const int r = coords[g] - geom[G_OZ + g];
+    return r < 0 ? 0 : (r >= trows ? trows - 1 : r);
+  }
+  if (mode == PACK3D_POS_PACKED_1D) return src;
+  return 0;
 }
 
 // Launchers (defined in the kernel sources).

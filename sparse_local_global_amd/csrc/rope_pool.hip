@@ -26,11 +26,11 @@ namespace {
 
 constexpr int kChunk = 64;  // tokens staged in LDS at a time
 
-__global__ void k_rope_table(float2* tab, int emax, int half, int da, double base) {
+__global__ void k_rope_table(float2* tab, int rows, int half, int gw, double base) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= emax * half) return;
+  if (i >= rows * half) return;
   const int c = i / half, k = i - c * half;
-  const double theta = pow(base, -2.0 * (double)k / (double)da);
+  const double theta = pow(base, -2.0 * (double)k / (double)gw);
   const double phi = (double)c * theta;
   tab[i] = make_float2((float)cos(phi), (float)sin(phi));
 }
@@ -50,16 +50,19 @@ struct RopeArgs {
   const int32_t* coords; const int32_t* perm; const int32_t* geom;
   const float2* tab;
   void* qrot; void* krot; void* vr; void* kbar; void* vbar;
-  int N, H, D, Dp, nblk, nblkp, bvol, heads_per_group, emax, half;
+  int N, H, D, Dp, nblk, nblkp, bvol, heads_per_group;
+  int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
 };
 
-template <typename T, int VEC>
+// GROUPS rotation groups of the head dim (3 axial, 1 packed 1D); ROTATE false: copy only.
+template <typename T, int VEC, int GROUPS, bool ROTATE>
 __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   extern __shared__ char smem[];
   const int blk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int N = a.N, H = a.H, D = a.D, Dp = a.Dp, bvol = a.bvol;
-  const int da = D / 3, half = a.half;
+  const int gw = D / GROUPS, half = gw / 2;
+  constexpr int groups = GROUPS;
   const int ntok = bvol < kChunk ? bvol : kChunk;
   const int nchunk = bvol / ntok;
   // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1], vl[ntok][Dp+1] (float)
@@ -75,11 +78,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
     const int src = a.perm[(int64_t)b * N + kappa];
     s_src[t] = src;
     const int32_t* c = a.coords + ((int64_t)b * N + src) * 3;
-    for (int ax = 0; ax < 3; ++ax) {
-      int r = c[ax] - g[G_OZ + ax];
-      r = r < 0 ? 0 : (r >= a.emax ? a.emax - 1 : r);  // in range whenever coords match the index
-      s_rel[t * 3 + ax] = r;
-    }
+    for (int gi = 0; gi < GROUPS; ++gi) s_rel[t * 3 + gi] = rope_row(a.pos_mode, gi, src, c, g, a.trows);
   }
   __syncthreads();
 
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   T* krot = (T*)a.krot;
   T* vr = (T*)a.vr;
   const int pchunks = half / VEC;         // VEC-wide pieces per half group
-  const int rope_items = ntok * 3 * pchunks;
+  const int rope_items = ntok * groups * pchunks;
   const int v_items = ntok * (D / VEC);
   const int h0 = hg * a.heads_per_group;
 
@@ -102,12 +101,12 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
       const int t0 = ch * ntok;
       // rotate q and k
       for (int it = tid; it < rope_items; it += 256) {
-        const int tok = it / (3 * pchunks);
-        const int rem = it - tok * 3 * pchunks;
-        const int ax = rem / pchunks, p = rem - ax * pchunks;
+        const int tok = it / (groups * pchunks);
+        const int rem = it - tok * groups * pchunks;
+        const int ax = rem / pchunks, p = rem - ax * pchunks;  // group, pair chunk
         const int src = s_src[t0 + tok];
         const int c = s_rel[(t0 + tok) * 3 + ax];
-        const int col1 = ax * da + p * VEC, col2 = col1 + half;
+        const int col1 = ax * gw + p * VEC, col2 = col1 + half;
         const int64_t in_row = ((int64_t)b * N + src) * H + h;
         const Vec<T, VEC> q1 = *(const Vec<T, VEC>*)(q + in_row * D + col1);
         const Vec<T, VEC> q2 = *(const Vec<T, VEC>*)(q + in_row * D + col2);
@@ -117,13 +116,14 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         const float2* cs = a.tab + (int64_t)c * half + p * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float2 r = cs[e];
+          // no rotation: the identity row (cos 1, sin 0), and x2 * 0 must not turn inf into NaN
+          const float2 r = ROTATE ? cs[e] : make_float2(1.f, 0.f);
           const float x1 = to_f(q1.v[e]), x2 = to_f(q2.v[e]);
-          oq1.v[e] = from_f<T>(x1 * r.x - x2 * r.y);
-          oq2.v[e] = from_f<T>(x1 * r.y + x2 * r.x);
+          oq1.v[e] = ROTATE ? from_f<T>(x1 * r.x - x2 * r.y) : q1.v[e];
+          oq2.v[e] = ROTATE ? from_f<T>(x1 * r.y + x2 * r.x) : q2.v[e];
           const float y1 = to_f(k1.v[e]), y2 = to_f(k2.v[e]);
-          const float ky1 = y1 * r.x - y2 * r.y;
-          const float ky2 = y1 * r.y + y2 * r.x;
+          const float ky1 = ROTATE ? y1 * r.x - y2 * r.y : y1;
+          const float ky2 = ROTATE ? y1 * r.y + y2 * r.x : y2;
           ok1.v[e] = from_f<T>(ky1);
           ok2.v[e] = from_f<T>(ky2);
           kl[tok * ls + col1 + e] = ky1;
@@ -183,23 +183,30 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   }
 }
 
+template <typename T, int GROUPS, bool ROTATE>
+void launch_mode(const Dims& d, const RopeArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  int vec = 1;
+  const int cap = 16 / (int)sizeof(T);
+  while (vec * 2 <= cap && d.half % (vec * 2) == 0) vec *= 2;
+  switch (vec) {
+    case 1: hipLaunchKernelGGL((k_rope_pool<T, 1, GROUPS, ROTATE>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_rope_pool<T, 2, GROUPS, ROTATE>), grid, dim3(256), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_rope_pool<T, 4, GROUPS, ROTATE>), grid, dim3(256), lds, s, a); break;
+    default:
+      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_rope_pool<T, 8, GROUPS, ROTATE>), grid, dim3(256), lds, s, a);
+      break;
+  }
+}
+
 template <typename T>
 pack3d_status launch_typed(const Dims& d, const RopeArgs& a, const char* name, hipStream_t s) {
   const int ntok = d.bvol < kChunk ? d.bvol : kChunk;
   const size_t lds = sizeof(int) * 4 * d.bvol + 2 * sizeof(float) * ntok * (d.Dp + 1);
   dim3 grid(d.nblk, d.H / a.heads_per_group, d.B);
   ProfileScope prof(name, s);
-  int vec = 1;
-  const int cap = 16 / (int)sizeof(T);
-  while (vec * 2 <= cap && d.half % (vec * 2) == 0) vec *= 2;
-  switch (vec) {
-    case 1: hipLaunchKernelGGL((k_rope_pool<T, 1>), grid, dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_rope_pool<T, 2>), grid, dim3(256), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_rope_pool<T, 4>), grid, dim3(256), lds, s, a); break;
-    default:
-      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((k_rope_pool<T, 8>), grid, dim3(256), lds, s, a);
-      break;
-  }
+  if (d.pos_mode == PACK3D_POS_AXIAL) launch_mode<T, 3, true>(d, a, grid, lds, s);
+  else if (d.pos_mode == PACK3D_POS_PACKED_1D) launch_mode<T, 1, true>(d, a, grid, lds, s);
+  else launch_mode<T, 1, false>(d, a, grid, lds, s);
   return check_launch("rope/pool");
 }
 
@@ -208,18 +215,18 @@ pack3d_status launch_typed(const Dims& d, const RopeArgs& a, const char* name, h
 pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack3d_attn* at,
                                const void* q, const void* k, const void* v, const int32_t* coords,
                                char* ws, const Workspace& w, const char* name, hipStream_t s) {
-  const int n_tab = d.emax * d.half;
+  const int n_tab = d.trows * d.half;
   {
     ProfileScope prof("rope_table", s);
     hipLaunchKernelGGL(k_rope_table, dim3((n_tab + 255) / 256), dim3(256), 0, s,
-                       (float2*)(ws + w.rope), d.emax, d.half, d.D / 3, (double)at->rope_base);
+                       (float2*)(ws + w.rope), d.trows, d.half, d.gw, (double)at->rope_base);
   }
   RopeArgs a;
   a.q = q; a.k = k; a.v = v; a.coords = coords; a.perm = ix->perm; a.geom = ix->geom;
   a.tab = (const float2*)(ws + w.rope);
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
   a.N = d.N; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
-  a.emax = d.emax; a.half = d.half;
+  a.pos_mode = d.pos_mode; a.groups = d.groups; a.gw = d.gw; a.half = d.half; a.trows = d.trows;
   // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all
   int hp = d.H;
   for (int c = 1; c <= d.H; ++c) {

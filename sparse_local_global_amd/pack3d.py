@@ -34,7 +34,7 @@ class Packing(ctypes.Structure):
 class Attn(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-                ("with_summaries", ctypes.c_int32)]
+                ("with_summaries", ctypes.c_int32), ("position_mode", ctypes.c_int32)]
 
 
 class Tables(ctypes.Structure):
@@ -177,11 +177,19 @@ def build_index(coords: torch.Tensor, block_shape, local_radius: int, order_hint
     return Index(handle, tables, b, n, block_shape, local_radius)
 
 
-def make_attn(dtype, heads, head_dim, rope_base=10000.0, scale=None, with_summaries=True) -> Attn:
+POSITION_MODES = {"axial": 0, "packed1d": 1, "none": 2}
+
+
+def make_attn(dtype, heads, head_dim, rope_base=10000.0, scale=None, with_summaries=True,
+              position_mode="axial") -> Attn:
+    """position_mode: "axial" (grid-coordinate RoPE, the method), "packed1d" (1D RoPE on the
+    packed position) or "none" (no rotation); the last two are controls."""
     if dtype not in _DTYPES:
         raise Pack3DError(E_UNSUPPORTED, f"dtype {dtype} is not supported")
+    if position_mode not in POSITION_MODES:
+        raise Pack3DError(E_INVALID, f"position_mode {position_mode!r} is not one of {sorted(POSITION_MODES)}")
     return Attn(_DTYPES[dtype], heads, head_dim, float(rope_base), 0.0 if scale is None else float(scale),
-                1 if with_summaries else 0)
+                1 if with_summaries else 0, POSITION_MODES[position_mode])
 
 
 def workspace_bytes(index: Index, attn: Attn, for_backward: bool = False) -> int:
@@ -194,11 +202,11 @@ def _check_act(name, t, shape, dtype):
 
 
 def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, with_summaries=True,
-            workspace: torch.Tensor | None = None, out=None, lse=None):
+            workspace: torch.Tensor | None = None, out=None, lse=None, position_mode="axial"):
     """PACK3D forward.  q, k, v [B, N, H, D]; returns (out [B, N, H, D], lse fp32 [B, H, N])."""
     lib = load_library()
     b, n, h, d = q.shape
-    attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries)
+    attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries, position_mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_act(name, t, (b, n, h, d), q.dtype)
     need = workspace_bytes(index, attn)
@@ -217,7 +225,8 @@ def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, wit
 
 
 def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0, scale=None,
-             with_summaries=True, workspace: torch.Tensor | None = None, reuse_forward: bool = False):
+             with_summaries=True, workspace: torch.Tensor | None = None, reuse_forward: bool = False,
+             position_mode="axial"):
     """Gradients (dq, dk, dv) of sum(out * dout) with respect to the unrotated q, k, v.
 
     reuse_forward=True: ``workspace`` is the one the forward of these inputs used (allocated
@@ -225,7 +234,7 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
     backward skips recomputing them."""
     lib = load_library()
     b, n, h, d = q.shape
-    attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries)
+    attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries, position_mode)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check_act(name, t, (b, n, h, d), q.dtype)
     need = workspace_bytes(index, attn, True)
@@ -243,10 +252,11 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
     return dq, dk, dv
 
 
-def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_base=10000.0) -> dict:
+def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_base=10000.0,
+                    position_mode="axial") -> dict:
     """Tensor views of the forward intermediates left in ``workspace``."""
     b, n, h, d = q_shape
-    attn = make_attn(dtype, h, d, rope_base)
+    attn = make_attn(dtype, h, d, rope_base, position_mode=position_mode)
     vw = Views()
     _check(load_library().pack3d_workspace_views(index.handle, ctypes.byref(attn), ctypes.byref(vw)))
     dp, nbp = vw.head_dim_padded, vw.nblk_padded
@@ -256,7 +266,7 @@ def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_
         cnt = math.prod(shape)
         return workspace[off: off + cnt * esize].view(dt).view(*shape)
 
-    half = d // 6
+    half = d // 6 if position_mode == "axial" else d // 2     # pairs per rotation group
     return dict(rope_table=view(vw.rope_table, (vw.extent_table, half, 2), torch.float32, 4),
                 qrot=view(vw.qrot, (b, h, n, dp)), krot=view(vw.krot, (b, h, n, dp)),
                 vrow=view(vw.vrow, (b, h, n, dp)), kbar=view(vw.kbar, (b, h, nbp, dp)),
@@ -291,33 +301,35 @@ class Pack3DAttention(torch.autograd.Function):
     """Autograd wrapper: forward and backward both run in libpack3d."""
 
     @staticmethod
-    def forward(ctx, q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True):
+    def forward(ctx, q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True,
+                position_mode="axial"):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         # the workspace is sized for the backward and kept, so the backward reuses the
         # forward's rotated and pooled operands instead of recomputing them
-        attn = make_attn(q.dtype, q.shape[2], q.shape[3], rope_base, scale, with_summaries)
+        attn = make_attn(q.dtype, q.shape[2], q.shape[3], rope_base, scale, with_summaries, position_mode)
         need = workspace_bytes(index, attn, True)
         if need == 0:
             raise Pack3DError(E_UNSUPPORTED, load_library().pack3d_last_error().decode())
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
         out, lse = forward(index, q, k, v, coords, rope_base=rope_base, scale=scale,
-                           with_summaries=with_summaries, workspace=ws)
+                           with_summaries=with_summaries, workspace=ws, position_mode=position_mode)
         ctx.save_for_backward(q, k, v, out, lse)
         ctx.index, ctx.coords, ctx.workspace = index, coords, ws
-        ctx.opts = (rope_base, scale, with_summaries)
+        ctx.opts = (rope_base, scale, with_summaries, position_mode)
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse = ctx.saved_tensors
-        rope_base, scale, with_summaries = ctx.opts
+        rope_base, scale, with_summaries, position_mode = ctx.opts
         dq, dk, dv = backward(ctx.index, q, k, v, ctx.coords, out, lse, dout.contiguous(), rope_base=rope_base,
                               scale=scale, with_summaries=with_summaries, workspace=ctx.workspace,
-                              reuse_forward=True)
+                              reuse_forward=True, position_mode=position_mode)
         ctx.workspace = None
-        return dq, dk, dv, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None
 
 
-def attention(q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True):
-    """PACK3D attention with autograd support."""
-    return Pack3DAttention.apply(q, k, v, index, coords, rope_base, scale, with_summaries)
+def attention(q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True,
+              position_mode="axial"):
+    """PACK3D attention with autograd support (position_mode: see make_attn)."""
+    return Pack3DAttention.apply(q, k, v, index, coords, rope_base, scale, with_summaries, position_mode)

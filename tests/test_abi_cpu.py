@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import sparse_local_global_amd.pack3d as p3
 
@@ -39,7 +40,7 @@ def test_exported_symbols_in_dynamic_table():
 
 def test_version_and_last_error():
     lib = p3.load_library()
-    assert lib.pack3d_version() == 101
+    assert lib.pack3d_version() == 102
     assert isinstance(lib.pack3d_last_error(), bytes)
 
 
@@ -92,3 +93,12 @@ def test_forward_argument_errors_return_codes():
     assert lib.pack3d_workspace_bytes(None, ctypes.byref(at), 0) == 0
     st = lib.pack3d_backward(None, ctypes.byref(at), *([None] * 10), None, 0, 0, None)
     assert st == p3.E_INVALID
+
+
+def test_position_mode_argument():
+    at = p3.make_attn(torch.bfloat16, 8, 96, position_mode="packed1d")
+    assert at.position_mode == 1
+    assert p3.make_attn(torch.float32, 2, 12).position_mode == 0
+    with pytest.raises(p3.Pack3DError) as e:
+        p3.make_attn(torch.float32, 2, 12, position_mode="sequence")
+    assert e.value.status == p3.E_INVALID
