@@ -463,7 +463,9 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
     }
   const int row = krow0 + kloc;
   const int src = a.perm[(int64_t)b * a.N + row];
-  if (qh == 0) {
+  // R^T on the lane's own pairs: every pair partner (+16 within an axis group, +48 for the
+  // 1D rotation) keeps the dim's residue mod 8, so it sits in the same lane
+  if (qh == 0 && a.pos_mode == PACK3D_POS_AXIAL) {
     const int32_t* g = a.geom + b * G_FIELDS;
     const int32_t* c = a.coords + ((int64_t)b * a.N + src) * 3;
 #pragma unroll
@@ -481,6 +483,17 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
           acc[dt][4 * j + 8 + e] = -lo * t.y + hi * t.x;  // -y1 s + y2 c
         }
     }
+  } else if (qh == 0 && a.pos_mode == PACK3D_POS_PACKED_1D) {
+    const float2* cs = a.tab + (int64_t)src * 48 + 4 * half;  // 48 pairs (k, k + 48) per row
+#pragma unroll
+    for (int m = 0; m < 6; ++m)  // dims 8m + 4 half + e and 8(m + 6) + 4 half + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 t = cs[8 * m + e];
+        const float y1 = acc[m / 4][4 * (m % 4) + e], y2 = acc[(m + 6) / 4][4 * ((m + 6) % 4) + e];
+        acc[m / 4][4 * (m % 4) + e] = y1 * t.x + y2 * t.y;
+        acc[(m + 6) / 4][4 * ((m + 6) % 4) + e] = -y1 * t.y + y2 * t.x;
+      }
   }
   bf16* dst = (bf16*)(qh == 0 ? a.dk : a.dv) + (((int64_t)b * a.N + src) * a.H + h) * 96;
 #pragma unroll
@@ -586,7 +599,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   constexpr int NDT = DP / 32;
   if constexpr (DP == 96) {
-    if (a.D == 96 && a.pos_mode == PACK3D_POS_AXIAL) {
+    if (a.D == 96) {
       local32_epilogue96(a, dk, dv, (f32x4*)(kh == 0 ? (void*)&s0 : (void*)&s1), b, h, kb, krow0, kloc, nk,
                          qh, lane, half);
       return;
@@ -703,6 +716,33 @@ __device__ inline void dq_epilogue96(const BwdArgs& a, f32x4 (&dq)[6], int b, in
   const int32_t* g = a.geom + b * G_FIELDS;
   const int32_t* c = a.coords + ((int64_t)b * a.N + src) * 3;
   T* dst = (T*)a.dq + (((int64_t)b * a.N + src) * a.H + h) * 96;
+  if (a.pos_mode == PACK3D_POS_PACKED_1D) {  // pairs (k, k + 48): dq[dt] with dq[dt + 3]
+    const float2* cs = a.tab + (int64_t)src * 48 + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+      Vec<T, 4> lo4, hi4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 t = cs[16 * dt + i];
+        const float lo = dq[dt][i] * a.scale, hi = dq[dt + 3][i] * a.scale;
+        lo4.v[i] = (T)(lo * t.x + hi * t.y);
+        hi4.v[i] = (T)(-lo * t.y + hi * t.x);
+      }
+      *(Vec<T, 4>*)(dst + 16 * dt + 4 * grp) = lo4;
+      *(Vec<T, 4>*)(dst + 48 + 16 * dt + 4 * grp) = hi4;
+    }
+    return;
+  }
+  if (a.pos_mode == PACK3D_POS_NONE) {
+#pragma unroll
+    for (int dt = 0; dt < 6; ++dt) {
+      Vec<T, 4> v4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4.v[i] = (T)(dq[dt][i] * a.scale);
+      *(Vec<T, 4>*)(dst + 16 * dt + 4 * grp) = v4;
+    }
+    return;
+  }
 #pragma unroll
   for (int ax = 0; ax < 3; ++ax) {
     int r = c[ax] - g[G_OZ + ax];
@@ -804,7 +844,7 @@ void k_bwd_dq(BwdArgs a) {
   };
   pipeline2(total, st0, st1, fetch, store, compute);
   if constexpr (DP == 96) {
-    if (a.D == 96 && a.pos_mode == PACK3D_POS_AXIAL) {
+    if (a.D == 96) {
       dq_epilogue96<T>(a, dq, b, h, qrow0 + qloc, qok, grp);
       return;
     }
