@@ -32,11 +32,23 @@ sequence position: the rotation of the RoPE section applied to the whole head
 dim, pairs (k, k + D/2), theta_k = base^(-2k/D), angle = packed index * theta_k)
 and "none" (no rotation).  Locality and summaries always follow the grid.
 
+Ragged geometry (``ragged=True``).  The abstract speaks of packed geometric
+data in general; a volume is then any set of distinct integer points (holes,
+extents that the block does not divide).  Plainest reading, used here: the
+block lattice is still anchored at the componentwise minimum and covers the
+bounding box with ceil(extent / b) blocks per axis; a block holds the tokens
+present in it; the local set is the present tokens of the blocks within the
+radius; every other *occupied* block gives one summary, the mean over the
+tokens present in it; an empty block gives none.  Canonical order keeps |b|
+slots per block, an absent point leaving its slot empty (perm = -1).  A batch
+of volumes with different token counts is passed flat ([T, H, D], coords
+[T, 3]) with ``offsets`` [B + 1]; lse is then [B, H, max N_v], NaN past N_v.
+
 Readings where the pages are silent (each listed in the design notes):
-block lattice anchored at each volume's componentwise minimum coordinate; only
-full grids with extents divisible by the block are accepted; no causal mask;
-V is not rotated; lse is the natural-log log-sum-exp of the scaled logits;
-gradients are taken with respect to the unrotated q, k, v.
+block lattice anchored at each volume's componentwise minimum coordinate; by
+default only full grids with extents divisible by the block are accepted; no
+causal mask; V is not rotated; lse is the natural-log log-sum-exp of the scaled
+logits; gradients are taken with respect to the unrotated q, k, v.
 """
 from __future__ import annotations
 
@@ -58,35 +70,41 @@ class CoordsError(ValueError):
 # Index: block membership, canonical order, neighbour table
 # --------------------------------------------------------------------------
 
-def _volume_index(c: np.ndarray, block, r: int, volume: int) -> dict:
-    """Tables of one volume.  ``c`` int [N, 3] (z, y, x)."""
+def _volume_index(c: np.ndarray, block, r: int, volume: int, ragged: bool = False) -> dict:
+    """Tables of one volume.  ``c`` int [N, 3] (z, y, x).
+
+    ``perm`` [nblk * |b|] maps a canonical slot to the packed position of its token, -1
+    for an empty slot (ragged geometry only); ``count`` [nblk] is the number of tokens
+    present in each block."""
     c = c.astype(np.int64)
     n = c.shape[0]
     b = np.asarray(block, dtype=np.int64)
+    if n == 0:
+        raise CoordsError(volume, "empty")
     origin = c.min(axis=0)
     extent = c.max(axis=0) - origin + 1
-    if int(np.prod(extent)) != n:
-        raise CoordsError(volume, "grid")
-    if np.any(extent % b):
-        raise CoordsError(volume, "divisible")
+    if not ragged:
+        if int(np.prod(extent)) != n:
+            raise CoordsError(volume, "grid")
+        if np.any(extent % b):
+            raise CoordsError(volume, "divisible")
     rel = c - origin
     # Duplicates: a token is offending when an earlier token has the same point.
-    lin = (rel[:, 0] * extent[1] + rel[:, 1]) * extent[2] + rel[:, 2]
-    first = np.full(n, n, dtype=np.int64)
-    np.minimum.at(first, lin, np.arange(n))
-    dup = np.nonzero(first[lin] != np.arange(n))[0]
+    _, first_idx, inv = np.unique(rel, axis=0, return_index=True, return_inverse=True)
+    dup = np.nonzero(first_idx[inv.reshape(-1)] != np.arange(n))[0]
     if dup.size:
         raise CoordsError(volume, "duplicate", int(dup.min()))
-    nb = extent // b
+    nb = -(-extent // b)                                    # ceil: partial edge blocks
     bvol = int(np.prod(b))
     beta = rel // b
     blk = (beta[:, 0] * nb[1] + beta[:, 1]) * nb[2] + beta[:, 2]
     w = rel - beta * b
     omega = (w[:, 0] * b[1] + w[:, 1]) * b[2] + w[:, 2]
     canon = blk * bvol + omega
-    perm = np.empty(n, dtype=np.int64)
-    perm[canon] = np.arange(n)
     nblk = int(np.prod(nb))
+    perm = np.full(nblk * bvol, -1, dtype=np.int64)
+    perm[canon] = np.arange(n)
+    count = np.bincount(blk, minlength=nblk)
     offsets = list(itertools.product(range(-r, r + 1), repeat=3))  # (dz, dy, dx) raster
     nbr = np.full((nblk, len(offsets)), -1, dtype=np.int64)
     for bid in range(nblk):
@@ -96,25 +114,37 @@ def _volume_index(c: np.ndarray, block, r: int, volume: int) -> dict:
             z, y, x = bz + dz, by + dy, bx + dx
             if 0 <= z < nb[0] and 0 <= y < nb[1] and 0 <= x < nb[2]:
                 nbr[bid, s] = (z * nb[1] + y) * nb[2] + x
-    return dict(origin=origin, extent=extent, nb=nb, nblk=nblk, bvol=bvol, block=b,
-                token_block=blk, canon=canon, perm=perm, nbr=nbr, radius=r)
+    return dict(origin=origin, extent=extent, nb=nb, nblk=nblk, bvol=bvol, block=b, n=n,
+                token_block=blk, canon=canon, perm=perm, count=count, present=perm >= 0, nbr=nbr,
+                radius=r)
 
 
-def build_index(coords, block_shape, local_radius: int) -> list:
-    """Per-volume tables for coords int [B, N, 3] (z, y, x).
+def split_volumes(x, offsets=None) -> list:
+    """Per-volume arrays: x [B, N, ...] (offsets None) or flat x [T, ...] cut at offsets [B + 1]."""
+    if offsets is None:
+        return [x[v] for v in range(x.shape[0])]
+    off = [int(o) for o in offsets]
+    if off[0] != 0 or any(b < a for a, b in zip(off, off[1:])) or off[-1] != x.shape[0]:
+        raise ValueError("offsets must start at 0, not decrease and end at the token count")
+    return [x[a:b] for a, b in zip(off, off[1:])]
 
-    Raises ``CoordsError`` for the first bad volume (holes / not a full grid,
-    extents not divisible by the block, duplicate points) and ``ValueError``
-    for a bad block shape or a negative radius.
+
+def build_index(coords, block_shape, local_radius: int, *, ragged: bool = False, offsets=None) -> list:
+    """Per-volume tables for coords int [B, N, 3] (z, y, x), or flat [T, 3] with ``offsets``.
+
+    Raises ``CoordsError`` for the first bad volume (without ``ragged``: not a full
+    grid, extents not divisible by the block; always: duplicate points, an empty
+    volume) and ``ValueError`` for a bad block shape or a negative radius.
     """
     coords = np.asarray(coords)
-    if coords.ndim == 2:
+    if coords.ndim == 2 and offsets is None:
         coords = coords[None]
     if len(block_shape) != 3 or min(block_shape) <= 0:
         raise ValueError("block_shape must hold three positive extents")
     if local_radius < 0:
         raise ValueError("local_radius must be >= 0")
-    return [_volume_index(coords[v], block_shape, int(local_radius), v) for v in range(coords.shape[0])]
+    return [_volume_index(c, block_shape, int(local_radius), v, ragged)
+            for v, c in enumerate(split_volumes(coords, offsets))]
 
 
 # --------------------------------------------------------------------------
@@ -200,15 +230,24 @@ def rotate(x, coords, packed_pos, base: float, mode: str, inverse: bool = False)
     raise ValueError(f"unknown position mode {mode!r}")
 
 
-def pool_blocks(x_canon: np.ndarray, bvol: int) -> np.ndarray:
-    """Mean over each block of a canonical-order array [N, ...] -> [nblk, ...]."""
+def pool_blocks(x_canon: np.ndarray, bvol: int, count=None) -> np.ndarray:
+    """Mean over the tokens present in each block of a canonical-order array [nblk * bvol, ...]
+    whose empty slots hold zeros -> [nblk, ...]; an empty block gives zeros."""
     n = x_canon.shape[0]
-    return x_canon.reshape(n // bvol, bvol, *x_canon.shape[1:]).mean(axis=1)
+    blocks = x_canon.reshape(n // bvol, bvol, *x_canon.shape[1:])
+    if count is None:
+        return blocks.mean(axis=1)
+    cnt = np.asarray(count, dtype=np.float64).reshape(-1, *([1] * (x_canon.ndim - 1)))
+    return np.divide(blocks.sum(axis=1), cnt, out=np.zeros_like(blocks[:, 0]), where=cnt > 0)
 
 
-def unpool_grad(dbar: np.ndarray, bvol: int) -> np.ndarray:
-    """Gradient of the block mean: every member of block b receives dbar_b / |b| (canonical order)."""
-    return np.repeat(dbar, bvol, axis=0) / bvol
+def unpool_grad(dbar: np.ndarray, bvol: int, count=None) -> np.ndarray:
+    """Gradient of the block mean: every member of block b receives dbar_b / n_b (canonical order;
+    n_b = |b| on a full grid, else the tokens present)."""
+    if count is None:
+        return np.repeat(dbar, bvol, axis=0) / bvol
+    cnt = np.maximum(np.asarray(count, dtype=np.float64), 1.0).reshape(-1, *([1] * (dbar.ndim - 1)))
+    return np.repeat(dbar / cnt, bvol, axis=0)
 
 
 # --------------------------------------------------------------------------
@@ -224,21 +263,32 @@ def _f64(t) -> np.ndarray:
     return np.asarray(t, dtype=np.float64)
 
 
-def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None, position_mode="axial"):
+def _canonical(x, perm, present):
+    """Rows of x [N, ...] in canonical order; empty slots hold zeros."""
+    out = np.zeros((perm.shape[0], *x.shape[1:]), dtype=np.float64)
+    out[present] = x[perm[present]]
+    return out
+
+
+def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None, position_mode="axial", ragged=False,
+             offsets=None):
     q, k, v = _f64(q), _f64(k), _f64(v)
     coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords)
-    if coords.ndim == 2:
+    if coords.ndim == 2 and offsets is None:
         coords = coords[None]
-    index = build_index(coords, block_shape, r)
+    index = build_index(coords, block_shape, r, ragged=ragged, offsets=offsets)
     rc = coords if rope_coords is None else np.asarray(rope_coords)
+    qs, ks, vs, rcs = (split_volumes(x, offsets) for x in (q, k, v, rc))
     vols = []
     for vi, ix in enumerate(index):
-        perm = ix["perm"]            # canonical slot -> packed position
-        qt = rotate(q[vi][perm], rc[vi][perm], perm, base, position_mode)
-        kt = rotate(k[vi][perm], rc[vi][perm], perm, base, position_mode)
-        vc = v[vi][perm]
+        perm, present = ix["perm"], ix["present"]       # canonical slot -> packed position (-1: empty)
+        pos = np.arange(ix["n"])
+        qt = _canonical(rotate(qs[vi], rcs[vi], pos, base, position_mode), perm, present)
+        kt = _canonical(rotate(ks[vi], rcs[vi], pos, base, position_mode), perm, present)
+        vc = _canonical(vs[vi], perm, present)
+        cnt = ix["count"] if ragged else None
         vols.append(dict(ix=ix, qt=qt, kt=kt, vc=vc,
-                         kbar=pool_blocks(kt, ix["bvol"]), vbar=pool_blocks(vc, ix["bvol"])))
+                         kbar=pool_blocks(kt, ix["bvol"], cnt), vbar=pool_blocks(vc, ix["bvol"], cnt)))
     return q, k, v, coords, vols
 
 
@@ -247,44 +297,121 @@ def _local_blocks(ix, qb):
 
 
 def _summary_blocks(ix, qb, local):
-    mask = np.ones(ix["nblk"], dtype=bool)
+    """Occupied blocks outside the local neighbourhood, in block-id order."""
+    mask = ix["count"] > 0
     mask[local] = False
     return np.nonzero(mask)[0]
 
 
-def _key_rows(local, bvol):
-    return np.concatenate([np.arange(n * bvol, (n + 1) * bvol) for n in local])
+def _key_rows(local, bvol, present=None):
+    rows = np.concatenate([np.arange(n * bvol, (n + 1) * bvol) for n in local])
+    return rows if present is None else rows[present[rows]]
+
+
+# --------------------------------------------------------------------------
+# Forward
+# --------------------------------------------------------------------------
+
+def _f64(t) -> np.ndarray:
+    """Exact conversion of a numpy array or a CPU torch tensor to fp64 numpy."""
+    if hasattr(t, "detach"):
+        t = t.detach().to("cpu")
+        import torch  # local: the oracle itself does not need torch
+        return t.to(torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def _canonical(x, perm, present):
+    """Rows of x [N, ...] in canonical order; empty slots hold zeros."""
+    out = np.zeros((perm.shape[0], *x.shape[1:]), dtype=np.float64)
+    out[present] = x[perm[present]]
+    return out
+
+
+def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None, position_mode="axial", ragged=False,
+             offsets=None):
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords)
+    if coords.ndim == 2 and offsets is None:
+        coords = coords[None]
+    index = build_index(coords, block_shape, r, ragged=ragged, offsets=offsets)
+    rc = coords if rope_coords is None else np.asarray(rope_coords)
+    qs, ks, vs, rcs = (split_volumes(x, offsets) for x in (q, k, v, rc))
+    vols = []
+    for vi, ix in enumerate(index):
+        perm, present = ix["perm"], ix["present"]       # canonical slot -> packed position (-1: empty)
+        pos = np.arange(ix["n"])
+        qt = _canonical(rotate(qs[vi], rcs[vi], pos, base, position_mode), perm, present)
+        kt = _canonical(rotate(ks[vi], rcs[vi], pos, base, position_mode), perm, present)
+        vc = _canonical(vs[vi], perm, present)
+        cnt = ix["count"] if ragged else None
+        vols.append(dict(ix=ix, qt=qt, kt=kt, vc=vc,
+                         kbar=pool_blocks(kt, ix["bvol"], cnt), vbar=pool_blocks(vc, ix["bvol"], cnt)))
+    return q, k, v, coords, vols
+
+
+def _local_blocks(ix, qb):
+    return [int(n) for n in ix["nbr"][qb] if n >= 0]
+
+
+def _summary_blocks(ix, qb, local):
+    """Occupied blocks outside the local neighbourhood, in block-id order."""
+    mask = ix["count"] > 0
+    mask[local] = False
+    return np.nonzero(mask)[0]
+
+
+def _key_rows(local, bvol, present=None):
+    rows = np.concatenate([np.arange(n * bvol, (n + 1) * bvol) for n in local])
+    return rows if present is None else rows[present[rows]]
+
+
+def _out_like(q, offsets, bsz, nmax, h):
+    """fp64 NaN outputs: o shaped like q, lse [B, H, max N_v]."""
+    return np.full(q.shape, np.nan), np.full((bsz, h, nmax), np.nan)
+
+
+def _join(parts, offsets):
+    """Per-volume arrays back to the caller's layout: stacked [B, N, ...] or flat [T, ...]."""
+    return np.stack(parts) if offsets is None else np.concatenate(parts)
 
 
 def forward(q, k, v, coords, block_shape, local_radius, *, rope_base=10000.0, scale=None,
             with_summaries=True, query_blocks=None, rope_coords=None, return_logits=False,
-            position_mode="axial"):
-    """PACK3D forward.  q, k, v [B, N, H, D]; coords [B, N, 3] (z, y, x).
+            position_mode="axial", ragged=False, offsets=None):
+    """PACK3D forward.  q, k, v [B, N, H, D]; coords [B, N, 3] (z, y, x); or, with
+    ``offsets`` [B + 1], flat q, k, v [T, H, D] and coords [T, 3].
 
-    Returns (o [B, N, H, D], lse [B, H, N]) in fp64, packed order.  With
-    ``query_blocks`` (a list of block ids) only those query blocks are
-    computed in every volume; other rows are NaN.  ``return_logits`` (tiny
-    inputs only) adds dense [B, H, N, N] local and [B, H, N, nblk] summary
-    logit matrices, NaN where a pair is not in the set.  ``position_mode`` picks the
-    rotation (see the module notes).
+    Returns (o, lse) in fp64, packed order: o shaped like q, lse [B, H, max N_v] (NaN
+    past a volume's token count).  With ``query_blocks`` (a list of block ids) only
+    those query blocks are computed in every volume; other rows are NaN.
+    ``return_logits`` (tiny uniform inputs only) adds dense [B, H, N, N] local and
+    [B, H, N, nblk] summary logit matrices, NaN where a pair is not in the set.
+    ``position_mode`` picks the rotation and ``ragged`` admits any set of distinct
+    points (see the module notes).
     """
     q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base, rope_coords,
-                                     position_mode)
-    bsz, n, h, d = q.shape
+                                     position_mode, ragged, offsets)
+    h, d = q.shape[-2], q.shape[-1]
+    bsz = len(vols)
+    nmax = max(vol["ix"]["n"] for vol in vols)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = np.full((bsz, n, h, d), np.nan)
-    lse = np.full((bsz, h, n), np.nan)
+    outs = [np.full((vol["ix"]["n"], h, d), np.nan) for vol in vols]
+    lse = np.full((bsz, h, nmax), np.nan)
     if return_logits:
-        lg_loc = np.full((bsz, h, n, n), np.nan)
-        lg_sum = np.full((bsz, h, n, vols[0]["ix"]["nblk"]), np.nan)
+        lg_loc = np.full((bsz, h, nmax, nmax), np.nan)
+        lg_sum = np.full((bsz, h, nmax, max(vol["ix"]["nblk"] for vol in vols)), np.nan)
     for vi, vol in enumerate(vols):
         ix = vol["ix"]
-        bvol, perm = ix["bvol"], ix["perm"]
-        qbs = range(ix["nblk"]) if query_blocks is None else query_blocks
+        bvol, perm, present = ix["bvol"], ix["perm"], ix["present"]
+        qbs = range(ix["nblk"]) if query_blocks is None else [qb for qb in query_blocks if qb < ix["nblk"]]
         for qb in qbs:
             rows = np.arange(qb * bvol, (qb + 1) * bvol)
+            rows = rows[present[rows]]
+            if rows.size == 0:
+                continue
             local = _local_blocks(ix, qb)
-            krows = _key_rows(local, bvol)
+            krows = _key_rows(local, bvol, present)
             qt = vol["qt"][rows].transpose(1, 0, 2)                          # [H, bq, D]
             s = scale * (qt @ vol["kt"][krows].transpose(1, 2, 0))           # [H, bq, nk]
             parts = [s]
@@ -302,13 +429,14 @@ def forward(q, k, v, coords, block_shape, local_radius, *, rope_base=10000.0, sc
                 acc = acc + et @ vol["vbar"][sb].transpose(1, 0, 2)
                 den = den + et.sum(-1, keepdims=True)
             src = perm[rows]                                                 # packed positions
-            o[vi, src] = (acc / den).transpose(1, 0, 2)
+            outs[vi][src] = (acc / den).transpose(1, 0, 2)
             lse[vi][:, src] = (m + np.log(den))[..., 0]
             if return_logits:
                 kp = perm[krows]
                 lg_loc[vi][:, src[:, None], kp[None, :]] = s
                 if use_sum:
                     lg_sum[vi][:, src[:, None], sb[None, :]] = t
+    o = _join(outs, offsets)
     if return_logits:
         return o, lse, lg_loc, lg_sum
     return o, lse
@@ -385,36 +513,37 @@ def dense_attention(q, k, v, coords, *, rope_base=10000.0, scale=None, position_
 # --------------------------------------------------------------------------
 
 def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.0, scale=None,
-             with_summaries=True, volumes=None, heads=None, position_mode="axial"):
-    """Gradients (dq, dk, dv) [B, N, H, D] fp64 of sum(o * do) w.r.t. unrotated q, k, v.
+             with_summaries=True, volumes=None, heads=None, position_mode="axial", ragged=False, offsets=None):
+    """Gradients (dq, dk, dv) fp64 of sum(o * do) w.r.t. unrotated q, k, v, shaped like q
+    (layouts as in ``forward``).
 
     With o_i = (sum_j P_ij V_j + sum_b P_ib Vbar_b), P = exp(logit - lse_i):
       delta_i = <dO_i, o_i>
       dS_ij = P_ij (<dO_i, V_j> - delta_i),  dT_ib = P_ib (<dO_i, Vbar_b> - delta_i)
       dQ~_i = scale (sum_j dS_ij K~_j + sum_b dT_ib Kbar_b)
-      dK~_j = scale sum_i dS_ij Q~_i + dKbar_b(j) / |b|,  dKbar_b = scale sum_i dT_ib Q~_i
-      dV_j  = sum_i P_ij dO_i + dVbar_b(j) / |b|,         dVbar_b = sum_i P_ib dO_i
-      dq = R(c)^T dQ~, dk = R(c)^T dK~  (the mean pooling broadcasts 1/|b| to its members).
+      dK~_j = scale sum_i dS_ij Q~_i + dKbar_b(j) / n_b,  dKbar_b = scale sum_i dT_ib Q~_i
+      dV_j  = sum_i P_ij dO_i + dVbar_b(j) / n_b,         dVbar_b = sum_i P_ib dO_i
+      dq = R(c)^T dQ~, dk = R(c)^T dK~  (the mean pooling broadcasts 1/n_b to the n_b
+      tokens present in block b; n_b = |b| on a full grid).
     ``volumes`` / ``heads`` restrict the work (other entries are NaN); R is the rotation of
     ``position_mode``.
     """
     q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base,
-                                     position_mode=position_mode)
-    do = _f64(do)
-    bsz, n, h, d = q.shape
+                                     position_mode=position_mode, ragged=ragged, offsets=offsets)
+    dos = split_volumes(_f64(do), offsets)
+    rcs = split_volumes(coords, offsets)
+    h, d = q.shape[-2], q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = np.full_like(q, np.nan)
-    dk = np.full_like(q, np.nan)
-    dv = np.full_like(q, np.nan)
-    vsel = range(bsz) if volumes is None else volumes
+    grads = [[np.full((vol["ix"]["n"], h, d), np.nan) for vol in vols] for _ in range(3)]
+    vsel = range(len(vols)) if volumes is None else volumes
     hsel = np.arange(h) if heads is None else np.asarray(heads)
     for vi in vsel:
         vol = vols[vi]
         ix = vol["ix"]
-        bvol, perm, nblk = ix["bvol"], ix["perm"], ix["nblk"]
+        bvol, perm, nblk, present = ix["bvol"], ix["perm"], ix["nblk"], ix["present"]
         qt_all, kt_all, vc_all = vol["qt"][:, hsel], vol["kt"][:, hsel], vol["vc"][:, hsel]
         kbar, vbar = vol["kbar"][:, hsel], vol["vbar"][:, hsel]
-        doc = do[vi][perm][:, hsel]
+        doc = _canonical(dos[vi], perm, present)[:, hsel]
         dqt = np.zeros_like(qt_all)
         dkt = np.zeros_like(kt_all)
         dvc = np.zeros_like(vc_all)
@@ -422,8 +551,11 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
         dvbar = np.zeros_like(vbar)
         for qb in range(nblk):
             rows = np.arange(qb * bvol, (qb + 1) * bvol)
+            rows = rows[present[rows]]
+            if rows.size == 0:
+                continue
             local = _local_blocks(ix, qb)
-            krows = _key_rows(local, bvol)
+            krows = _key_rows(local, bvol, present)
             qt = qt_all[rows].transpose(1, 0, 2)                 # [H, bq, D]
             kk = kt_all[krows].transpose(1, 0, 2)                # [H, nk, D]
             vv = vc_all[krows].transpose(1, 0, 2)
@@ -448,7 +580,7 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
             delta = (dob * ob).sum(-1, keepdims=True)            # [H, bq, 1]
             ds = p * (dob @ vv.transpose(0, 2, 1) - delta)
             dqb = ds @ kk
-            # krows lists each neighbour block once, so fancy-index accumulation is exact
+            # krows lists each key once, so fancy-index accumulation is exact
             dkt[krows] += (scale * ds.transpose(0, 2, 1) @ qt).transpose(1, 0, 2)
             dvc[krows] += (p.transpose(0, 2, 1) @ dob).transpose(1, 0, 2)
             if use_sum:
@@ -457,13 +589,16 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
                 dkbar[sb] += (scale * dt.transpose(0, 2, 1) @ qt).transpose(1, 0, 2)
                 dvbar[sb] += (pt.transpose(0, 2, 1) @ dob).transpose(1, 0, 2)
             dqt[rows] = scale * dqb.transpose(1, 0, 2)
-        dkt += unpool_grad(dkbar, bvol)
-        dvc += unpool_grad(dvbar, bvol)
-        c = coords[vi][perm]
-        dq_c = rotate(dqt, c, perm, rope_base, position_mode, inverse=True)
-        dk_c = rotate(dkt, c, perm, rope_base, position_mode, inverse=True)
-        for src, dst in ((dq_c, dq), (dk_c, dk), (dvc, dv)):
-            tmp = np.empty((n, len(hsel), d))
-            tmp[perm] = src
-            dst[vi][:, hsel] = tmp
-    return dq, dk, dv
+        cnt = ix["count"] if ragged else None
+        dkt += unpool_grad(dkbar, bvol, cnt)
+        dvc += unpool_grad(dvbar, bvol, cnt)
+        live = np.nonzero(present)[0]                            # canonical slots holding a token
+        src = perm[live]
+        c = rcs[vi][src]
+        dq_c = rotate(dqt[live], c, src, rope_base, position_mode, inverse=True)
+        dk_c = rotate(dkt[live], c, src, rope_base, position_mode, inverse=True)
+        for g, val in zip(grads, (dq_c, dk_c, dvc[live])):
+            tmp = np.full((ix["n"], len(hsel), d), np.nan)
+            tmp[src] = val
+            g[vi][:, hsel] = tmp
+    return tuple(_join(g, offsets) for g in grads)

@@ -157,3 +157,45 @@ def small_workload(grid=(4, 6, 8), block=(2, 2, 2), heads=2, head_dim=12, radius
     """An ad-hoc small workload for tests."""
     return Workload(f"small{grid}", batch, tuple(grid), packing, heads, head_dim, tuple(block), radius,
                     (torch.float32,), seed=seed, input_scale=input_scale, rope_base=rope_base)
+
+
+def make_ragged_inputs(grids, heads, head_dim, dtype=torch.float32, *, occupancy=1.0, seed=0, with_grad=False,
+                       shifts=None, input_scale=1.0):
+    """Seeded ragged batch, flat in packed order (tokens of volume v at offsets[v]:offsets[v+1]).
+
+    Volume v holds the points of a ``grids[v]`` box (any extents), each kept with
+    probability ``occupancy`` (the box corners always, so the extents are exact), moved
+    by ``shifts[v]``, in a random packing order.  Values are N(0, 1) (times
+    ``input_scale``) drawn per kept point in raster order.
+
+    keys: q, k, v (and do) [T, H, D] in ``dtype``; coords int32 [T, 3]; offsets int64
+    [B + 1]; raster int64 [T] (raster index of each token inside its box).
+    """
+    rng = np.random.default_rng(seed)
+    qs, ks, vs, dos, cs, rs, offs = [], [], [], [], [], [], [0]
+    for v, grid in enumerate(grids):
+        rc = raster_coords(grid).astype(np.int64)
+        keep = rng.random(rc.shape[0]) < occupancy
+        hi = np.asarray(grid) - 1
+        corner = ((rc == 0) | (rc == hi)).all(axis=1)
+        keep |= corner
+        idx = np.nonzero(keep)[0]
+        order = rng.permutation(idx.shape[0])
+        idx = idx[order]
+        n = idx.shape[0]
+        shift = np.zeros(3, dtype=np.int64) if shifts is None else np.asarray(shifts[v], dtype=np.int64)
+        cs.append((rc[idx] + shift).astype(np.int32))
+        rs.append(idx)
+        for lst in (qs, ks, vs):
+            full = _draw(rng, (rc.shape[0], heads, head_dim), input_scale, dtype)
+            lst.append(full[torch.from_numpy(idx)])
+        if with_grad:
+            full = _draw(np.random.default_rng(seed + 2000 + v), (rc.shape[0], heads, head_dim), 1.0, dtype)
+            dos.append(full[torch.from_numpy(idx)])
+        offs.append(offs[-1] + n)
+    out = {"q": torch.cat(qs).contiguous(), "k": torch.cat(ks).contiguous(), "v": torch.cat(vs).contiguous(),
+           "coords": torch.from_numpy(np.concatenate(cs)).contiguous(),
+           "offsets": torch.tensor(offs, dtype=torch.int64), "raster": torch.from_numpy(np.concatenate(rs))}
+    if with_grad:
+        out["do"] = torch.cat(dos).contiguous()
+    return out

@@ -42,7 +42,7 @@ def _q0_closed_form_error(w):
 def test_sum_instead_of_mean_pooling_fails_closed_form(monkeypatch):
     w = _w()
     assert _q0_closed_form_error(w) < 1e-13
-    monkeypatch.setattr(op, "pool_blocks", lambda x, b: x.reshape(x.shape[0] // b, b, *x.shape[1:]).sum(1))
+    monkeypatch.setattr(op, "pool_blocks", lambda x, b, count=None: x.reshape(x.shape[0] // b, b, *x.shape[1:]).sum(1))
     assert _q0_closed_form_error(w) > 1e-3
 
 
@@ -102,7 +102,7 @@ def test_dropped_pooling_gradient_fails_autograd(monkeypatch):
     dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, 1)
     assert np.abs(dk[0] - k.grad.numpy()).max() < 1e-12
     # plant: the summary gradients are never broadcast back to the block members
-    monkeypatch.setattr(op, "unpool_grad", lambda dbar, bvol: np.zeros((dbar.shape[0] * bvol,) + dbar.shape[1:]))
+    monkeypatch.setattr(op, "unpool_grad", lambda dbar, bvol, count=None: np.zeros((dbar.shape[0] * bvol,) + dbar.shape[1:]))
     dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, 1)
     assert np.abs(dk[0] - k.grad.numpy()).max() > 1e-6 and np.abs(dv[0] - v.grad.numpy()).max() > 1e-6
 
@@ -163,3 +163,48 @@ def test_negative_control_lattice_anchored_at_zero_breaks_shift_invariance():
     ia = oracle.build_index(c[None], tuple(block), 1)[0]
     ib = oracle.build_index(shifted[None], tuple(block), 1)[0]
     assert np.array_equal(ia["token_block"], ib["token_block"])
+
+
+# ---- ragged geometry -------------------------------------------------------------
+
+def _ragged_naive_error():
+    x = si.make_ragged_inputs([(5, 6, 7)], 2, 12, occupancy=0.6, seed=61)
+    args = (x["q"][None], x["k"][None], x["v"][None], x["coords"][None], (2, 2, 2), 1)
+    o, _ = oracle.forward(*args, ragged=True)
+    o2, _ = oracle.forward_naive(*args)
+    return np.abs(o - o2).max()
+
+
+def test_pooling_over_whole_block_volume_fails_ragged_definition(monkeypatch):
+    """Dividing a partial block's sum by |b| instead of the tokens present."""
+    assert _ragged_naive_error() < 1e-12
+    orig = op.pool_blocks
+    monkeypatch.setattr(op, "pool_blocks", lambda x, b, count=None: orig(x, b))
+    assert _ragged_naive_error() > 1e-3
+
+
+def test_empty_block_summaries_fail_ragged_definition(monkeypatch):
+    """Giving empty blocks a (zero) summary logit."""
+    monkeypatch.setattr(op, "_summary_blocks",
+                        lambda ix, qb, local: np.setdiff1d(np.arange(ix["nblk"]), np.asarray(local, dtype=np.int64)))
+    assert _ragged_naive_error() > 1e-3
+
+
+def test_absent_keys_left_in_local_set_fail_ragged_definition(monkeypatch):
+    """Keeping the empty slots of the local blocks as (zero) keys."""
+    orig = op._key_rows
+    monkeypatch.setattr(op, "_key_rows", lambda local, bvol, present=None: orig(local, bvol))
+    assert _ragged_naive_error() > 1e-3
+
+
+def test_unpool_by_block_volume_fails_ragged_autograd(monkeypatch):
+    from tests.dense_ref import dense_masked
+    x = si.make_ragged_inputs([(5, 4, 7)], 2, 12, occupancy=0.7, seed=62, with_grad=True)
+    orig = op.unpool_grad
+    monkeypatch.setattr(op, "unpool_grad", lambda dbar, bvol, count=None: orig(dbar, bvol))
+    _, dk, _ = oracle.backward(x["q"][None], x["k"][None], x["v"][None], x["coords"][None], x["do"][None],
+                               (2, 2, 3), 1, ragged=True, position_mode="none")
+    q, k, v = (x[n].double().clone().requires_grad_() for n in ("q", "k", "v"))
+    o = dense_masked(q, k, v, x["coords"].long(), (2, 2, 3), 1, lambda t: t)
+    (o * x["do"].double()).sum().backward()
+    assert np.abs(dk[0] - k.grad.numpy()).max() > 1e-4

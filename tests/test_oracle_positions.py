@@ -21,6 +21,7 @@ import torch
 import oracle
 import oracle.pack3d as op
 import synthetic_inputs as si
+from tests.dense_ref import dense_masked
 
 
 def _complex_rope_1d(x, pos, base):
@@ -141,32 +142,6 @@ def test_repacking_axial_and_none_equivariant_packed1d_not():
     assert np.abs(res[("random", "packed1d")] - res[("raster", "packed1d")]).max() > 1e-2
 
 
-def _dense_masked(q, k, v, c, block, r, rot, with_summaries=True):
-    """Independent dense-masked formulation (torch, fp64): pooling as an averaging matrix and
-    one softmax over [local keys | summaries]; rot(x) applies the rotation."""
-    n, h, d = q.shape
-    cc = c - c.min(0).values
-    bc = cc // torch.tensor(block)
-    keys, inv = torch.unique(bc, dim=0, return_inverse=True)
-    pool = torch.zeros(keys.shape[0], n, dtype=torch.float64)
-    pool[inv, torch.arange(n)] = 1.0
-    pool = pool / pool.sum(1, keepdim=True)
-    loc = (bc[:, None, :] - bc[None, :, :]).abs().amax(-1) <= r
-    far = (bc[:, None, :] - keys[None, :, :]).abs().amax(-1) > r
-    if not with_summaries:
-        far = torch.zeros_like(far)
-    qt, kt = rot(q), rot(k)
-    kbar = torch.einsum("bn,nhd->bhd", pool, kt)
-    vbar = torch.einsum("bn,nhd->bhd", pool, v)
-    s = torch.einsum("ihd,jhd->hij", qt, kt) / math.sqrt(d)
-    t = torch.einsum("ihd,bhd->hib", qt, kbar) / math.sqrt(d)
-    s = s.masked_fill(~loc[None], float("-inf"))
-    t = t.masked_fill(~far[None], float("-inf"))
-    p = torch.softmax(torch.cat([s, t], -1), -1)
-    vals = torch.cat([v.transpose(0, 1), vbar.transpose(0, 1)], 1)
-    return (p @ vals).transpose(0, 1)
-
-
 def _torch_rope_1d(x, base):
     """1D RoPE at positions 0..N-1 through torch complex arithmetic."""
     n, h, d = x.shape
@@ -185,7 +160,7 @@ def test_backward_against_autograd(mode):
     dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, 1, position_mode=mode)
     rot = (lambda t: t) if mode == "none" else (lambda t: _torch_rope_1d(t, 10000.0))
     q, k, v = (x[n][0].double().clone().requires_grad_() for n in ("q", "k", "v"))
-    o = _dense_masked(q, k, v, x["coords"][0].long(), w.block, 1, rot)
+    o = dense_masked(q, k, v, x["coords"][0].long(), w.block, 1, rot)
     (o * x["do"][0].double()).sum().backward()
     for g, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
         np.testing.assert_allclose(g[0], ref.numpy(), atol=1e-11)
