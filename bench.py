@@ -99,6 +99,44 @@ def gemm_ceiling(steps: int = 20, n: int = 8192) -> dict:
             "library": "torch.matmul (hipBLASLt), bf16 in, fp32 accumulate"}
 
 
+def ragged_step(name: str, steps: int, warmup: int) -> dict:
+    """Forward + backward step on a ragged varlen batch (partial edge blocks, holes, two volume
+    shapes), timed like the headline step; per-kernel averages from the library's events."""
+    import torch
+    import synthetic_inputs as si
+    import sparse_local_global_amd.pack3d as p3
+    spec = si.RAGGED_WORKLOADS[name]
+    x = si.make_ragged_inputs(spec["grids"], spec["heads"], spec["head_dim"], torch.bfloat16,
+                              occupancy=spec["occupancy"], seed=spec["seed"], with_grad=True)
+    off = x["offsets"].tolist()
+    xd = {k: v.to("cuda:0") for k, v in x.items() if k in ("q", "k", "v", "coords", "do")}
+    ix = p3.build_index(xd["coords"], spec["block"], spec["radius"], ragged=True, offsets=off)
+    attn = p3.make_attn(torch.bfloat16, spec["heads"], spec["head_dim"])
+    ws = torch.empty(p3.workspace_bytes(ix, attn, True), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(xd["q"])
+    lse = torch.empty((ix.batch, spec["heads"], ix.tokens), dtype=torch.float32, device="cuda:0")
+
+    def step():
+        p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], workspace=ws, out=out, lse=lse)
+        p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws,
+                    reuse_forward=True)
+
+    for _ in range(warmup):
+        step()
+    ms = time_region(step, steps)
+    p3.profile_reset()
+    p3.profile_enable(True)
+    time_region(step, steps)
+    prof = p3.profile_read()
+    p3.profile_enable(False)
+    t = ix.tables()
+    tokens = off[-1]
+    return {"workload": name, "description": spec["description"], "tokens": tokens,
+            "canonical_slots": ix.batch * t["nblk"] * t["block_tokens"], "ms_per_step": ms,
+            "tokens_per_s": tokens / (ms * 1e-3), "pass": "forward+backward",
+            "kernels_avg_ms": {k: tt / max(n, 1) for k, (n, tt) in prof.items()}}
+
+
 def cpu_baseline(w, x, sample_blocks: int) -> dict:
     """The fp64 oracle on the host cores: all heads of the first `sample_blocks` query blocks of each volume."""
     import oracle  # test infrastructure, used only for this reported baseline
@@ -121,14 +159,16 @@ def cpu_baseline(w, x, sample_blocks: int) -> dict:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="65k")
     ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
     ap.add_argument("--position-mode", default="axial", choices=["axial", "packed1d", "none"],
                     help="rotation of the timed step (axial grid-coordinate RoPE is the method)")
     ap.add_argument("--no-mode-compare", action="store_true",
                     help="skip timing the step under the other position modes")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip timing the step on the ragged varlen stand-in (partial blocks, holes)")
     ap.add_argument("--cpu-sample-blocks", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true", help="skip the hipBLASLt GEMM reference")
@@ -305,6 +345,10 @@ def main(argv=None) -> int:
     }
     if modes:
         result["position_modes"] = modes
+    if not args.no_ragged and with_bwd:
+        rg = ragged_step("65k-ragged", args.steps, args.warmup)
+        log(f"bench: ragged 65k-ragged: step {rg['ms_per_step']:.3f} ms ({rg['tokens']} tokens)")
+        result["ragged"] = rg
     if not args.no_gemm_ceiling:
         g = gemm_ceiling()
         result["gemm_ceiling"] = g

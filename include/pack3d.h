@@ -13,12 +13,16 @@
  *   - Every pointer named *_dev is device memory owned by the caller; the library
  *     never allocates, frees or retains device memory.  It allocates only the small
  *     host-side index handle (malloc/free).
- *   - q, k, v, out, dout, dq, dk, dv are contiguous [B, N, H, D] arrays, D innermost,
- *     in packed (caller) order, all of the dtype named in pack3d_attn.  lse is fp32
- *     [B, H, N] in packed order.  coords is int32 [B, N, 3] holding (z, y, x).
+ *   - q, k, v, out, dout, dq, dk, dv are contiguous [T, H, D] arrays, D innermost,
+ *     in packed (caller) order, all of the dtype named in pack3d_attn: volume v owns
+ *     tokens off[v] .. off[v+1]-1 (uniform layout: off[v] = v N, i.e. [B, N, H, D]).
+ *     lse is fp32 [B, H, Nmax] in packed order inside each volume (Nmax = the largest
+ *     volume; entries past a volume's token count are not written).  coords is int32
+ *     [T, 3] holding (z, y, x).
  *   - stream is a hipStream_t (NULL = the null stream).  Forward and backward are
  *     asynchronous on it and never synchronize.  pack3d_build_index synchronizes the
- *     stream once (to read back the geometry check).
+ *     stream once (twice for ragged geometry) to read back the geometry check;
+ *     pack3d_measure_blocks synchronizes it once.
  *   - On any error nothing is launched (argument errors) and a message is kept in a
  *     thread-local buffer returned by pack3d_last_error().  Launch failures return
  *     PACK3D_E_HIP.
@@ -38,8 +42,9 @@ extern "C" {
 typedef enum pack3d_status {
   PACK3D_OK = 0,
   PACK3D_E_INVALID = 1,     /* null pointer, non-positive size, bad radius or block shape */
-  PACK3D_E_COORDS = 2,      /* geometry rejected: not a full grid, extents not divisible
-                               by the block, or a duplicate point */
+  PACK3D_E_COORDS = 2,      /* geometry rejected: not a full grid or extents not divisible
+                               by the block (without ragged), a duplicate point, an empty
+                               volume, more blocks than the tables were sized for */
   PACK3D_E_UNSUPPORTED = 3, /* valid request outside what the kernels implement */
   PACK3D_E_WORKSPACE = 4,   /* caller buffer smaller than the size query returned */
   PACK3D_E_HIP = 5          /* HIP runtime or launch error */
@@ -56,11 +61,32 @@ typedef enum pack3d_order {
   PACK3D_ORDER_RANDOM = 4
 } pack3d_order;
 
-/* Batch layout: `batch` volumes of `tokens_per_volume` tokens each. */
+/* Batch layout and geometry class.
+ *   batch:             number of volumes B.
+ *   tokens_per_volume: uniform layout (volume_offsets NULL): tokens N of every volume.
+ *                      Ignored with volume_offsets.
+ *   order_hint:        pack3d_order.
+ *   ragged:            0: every volume must be a full grid (N = product of its extents)
+ *                      whose extents the block divides (PACK3D_E_COORDS otherwise).
+ *                      1: a volume is any set of distinct integer points: partial edge
+ *                      blocks and holes ("Geometry Matters in Packed 3D Attention",
+ *                      abstract: packed geometric data).  Blocks cover each volume's
+ *                      bounding box from its minimum corner (ceil(extent / b) per axis);
+ *                      the local set is the tokens present in the blocks within the
+ *                      radius; each other occupied block gives one summary, the mean
+ *                      over its tokens; an empty block gives none.
+ *   volume_offsets:    NULL, or a host array of batch + 1 token offsets (off[0] = 0,
+ *                      non-decreasing, every volume non-empty) for volumes of different
+ *                      token counts (varlen batch); read during the call only.
+ *   max_blocks:        ragged only: blocks per volume the index tables are sized for
+ *                      (pack3d_measure_blocks gives the exact need).  Ignored otherwise. */
 typedef struct pack3d_packing {
   int32_t batch;
   int32_t tokens_per_volume;
   int32_t order_hint; /* pack3d_order */
+  int32_t ragged;
+  const int32_t* volume_offsets;
+  int32_t max_blocks;
 } pack3d_packing;
 
 /* Angle source of the rotation ("Geometry Matters in Packed 3D Attention", abstract: the
@@ -101,16 +127,22 @@ typedef struct pack3d_attn {
 typedef struct pack3d_index pack3d_index;
 
 /* Device views of the index tables (read-only; they live in the caller's tables_dev).
- *   token_block [B, N]      block id of each packed token; blocks are numbered in raster
+ * nblk is the largest block count of the batch; a volume with fewer blocks has empty
+ * ones past its own count.  Local indices count tokens inside a volume.
+ *   token_block [T]         block id of each packed token; blocks are numbered in raster
  *                           order over the block grid (z slowest) of its volume
- *   canon       [B, N]      canonical slot of each packed token: block id * |b| + raster
+ *   canon       [T]         canonical slot of each packed token: block id * |b| + raster
  *                           offset inside the block
- *   perm        [B, N]      packed index stored at each canonical slot (inverse of canon)
+ *   perm        [B, nblk |b|]  local packed index stored at each canonical slot (inverse
+ *                           of canon), -1 for an empty slot
  *   nbr         [B, nblk, slots]  block ids of the (2r+1)^3 neighbourhood of each block,
  *                           slots in raster order over (dz, dy, dx) in [-r, r]^3, -1 outside
- *                           the volume
- *   geom        [B, 8]      origin (z, y, x) = componentwise minimum coordinate, extent
- *                           (z, y, x), status, offending token (device copy)          */
+ *                           the volume's block grid (a whole row of -1 past its blocks)
+ *   block_count [B, nblk]   tokens present in each block
+ *   volume_offsets [B + 1]  token offset of each volume
+ *   geom        [B, 10]     origin (z, y, x) = componentwise minimum coordinate, extent
+ *                           (z, y, x), status, offending token, tokens, blocks of the
+ *                           volume (device copy)                                       */
 typedef struct pack3d_tables {
   const int32_t* token_block;
   const int32_t* canon;
@@ -120,16 +152,29 @@ typedef struct pack3d_tables {
   int32_t batch, tokens, nblk, block_tokens, slots, radius;
   int32_t block_shape[3];
   int32_t extent_max[3];
+  const int32_t* block_count;
+  const int32_t* volume_offsets;
+  int64_t total_tokens;
+  int32_t ragged, holes; /* holes: some canonical slot is empty */
 } pack3d_tables;
 
 /* Device bytes needed for the index tables of this batch layout, block shape and
- * radius; 0 if the arguments are invalid.  The count does not depend on the
- * coordinates: a valid geometry has exactly N / |b| blocks per volume. */
+ * radius; 0 if the arguments are invalid.  Without ragged the count follows from the
+ * token counts (a valid volume has N_v / |b| blocks); with ragged it is sized for
+ * packing->max_blocks blocks per volume. */
 size_t pack3d_index_bytes(const pack3d_packing* packing, const int32_t block_shape[3],
                           int32_t local_radius);
 
+/* Ragged geometry: the number of blocks per volume (the largest over the batch) that the
+ * coordinates need, i.e. the product over the axes of ceil(extent / b), into
+ * *max_blocks_out.  scratch_dev: device buffer of at least 64 * batch bytes.  Runs on the
+ * stream and synchronizes it once.  PACK3D_E_COORDS for an empty volume. */
+pack3d_status pack3d_measure_blocks(const int32_t* coords_dev, const pack3d_packing* packing,
+                                    const int32_t block_shape[3], void* scratch_dev,
+                                    size_t scratch_bytes, void* stream, int32_t* max_blocks_out);
+
 /* Build the index of a batch of packed volumes.
- *   coords_dev [B, N, 3] int32 (z, y, x) grid coordinates in packed order.
+ *   coords_dev [T, 3] int32 (z, y, x) grid coordinates in packed order.
  *   block_shape (bz, by, bx) >= 1 with bz*by*bx a multiple of 8; local_radius r in
  *   block units (0 <= r <= 7): a query's local set is every key whose block is within
  *   Chebyshev distance r of the query's block (truncated at the volume edge); every
@@ -138,8 +183,9 @@ size_t pack3d_index_bytes(const pack3d_packing* packing, const int32_t block_sha
  *   it must outlive the handle.
  * Each volume's block lattice is anchored at its componentwise minimum coordinate.
  * Rejected with PACK3D_E_COORDS (message names the volume and, for a duplicate, the
- * lowest packed index whose point already occurs earlier): extents whose product is
- * not N (holes), extents not divisible by the block, duplicate points.
+ * lowest local index whose point already occurs earlier in the volume): without ragged,
+ * extents whose product is not N (holes) or that the block does not divide; always,
+ * duplicate points; with ragged, more blocks than packing->max_blocks.
  * On success *out receives a handle to release with pack3d_index_free. */
 pack3d_status pack3d_build_index(const int32_t* coords_dev, const pack3d_packing* packing,
                                  const int32_t block_shape[3], int32_t local_radius,
@@ -149,7 +195,8 @@ pack3d_status pack3d_build_index(const int32_t* coords_dev, const pack3d_packing
 /* Fill *out with device views of the tables and their sizes. */
 pack3d_status pack3d_index_tables(const pack3d_index* index, pack3d_tables* out);
 
-/* Host copy of one volume's origin and extent: out6 = (oz, oy, ox, ez, ey, ex). */
+/* Host copy of one volume's origin and extent: out6 = (oz, oy, ox, ez, ey, ex) (the extent
+ * of the coordinates' bounding box). */
 pack3d_status pack3d_index_geometry(const pack3d_index* index, int32_t volume, int32_t out6[6]);
 
 void pack3d_index_free(pack3d_index* index);
@@ -158,7 +205,7 @@ void pack3d_index_free(pack3d_index* index);
  * (for_backward = 1); 0 if the request is invalid or unsupported. */
 size_t pack3d_workspace_bytes(const pack3d_index* index, const pack3d_attn* attn, int for_backward);
 
-/* Forward.  Writes out [B, N, H, D] (attn->dtype) and lse [B, H, N] fp32: lse is the
+/* Forward.  Writes out [T, H, D] (attn->dtype) and lse [B, H, Nmax] fp32: lse is the
  * natural-log log-sum-exp of the scaled local and summary logits of each query.
  * coords_dev must hold the coordinates the index was built from: the RoPE angles
  * are taken from them (relative to each volume's origin, which leaves every logit
@@ -170,8 +217,9 @@ pack3d_status pack3d_forward(const pack3d_index* index, const pack3d_attn* attn,
                              const int32_t* coords_dev, void* out_dev, float* lse_dev,
                              void* workspace_dev, size_t workspace_bytes, void* stream);
 
-/* Backward of sum(out * dout): gradients dq, dk, dv [B, N, H, D] (attn->dtype) with
- * respect to the unrotated q, k, v, through the RoPE and the block mean pooling.
+/* Backward of sum(out * dout): gradients dq, dk, dv [T, H, D] (attn->dtype) with
+ * respect to the unrotated q, k, v, through the RoPE and the block mean pooling (a
+ * block's mean spreads 1/n_b to each of its n_b present tokens).
  * out_dev and lse_dev are the forward's outputs for the same inputs.  The workspace
  * needs pack3d_workspace_bytes(index, attn, 1) bytes; its first
  * pack3d_workspace_bytes(index, attn, 0) bytes have the forward's layout.
@@ -190,14 +238,16 @@ pack3d_status pack3d_backward(const pack3d_index* index, const pack3d_attn* attn
 
 /* Where the forward leaves its intermediates inside the workspace (byte offsets),
  * for inspection by tests.  All arrays are in canonical order (block-major, raster
- * inside each block), elements of attn->dtype except rope_table (float2 cos, sin).
+ * inside each block; empty slots hold zero rows), elements of attn->dtype except
+ * rope_table (float2 cos, sin).  N below is nblk * |b| canonical rows per volume.
  *   rope_table [extent_table, P]     cos and sin of angle row r, pair k; P = D/6 pairs per
  *                                    axis group (axial), D/2 (packed 1D) or D/2 with the
  *                                    single row 0 (no rotation)
  *   qrot, krot, vrow [B, H, N, Dp]   rotated Q and K, and V, rows zero-padded to Dp
- *   kbar, vbar [B, H, nblk_pad, Dp]  block means of the rotated K and of V (zero padding rows)
+ *   kbar, vbar [B, H, nblk_pad, Dp]  block means (over present tokens) of the rotated K and
+ *                                    of V (zero rows for empty and padding blocks)
  * Axial rotation angles use coordinates relative to each volume's origin (rows =
- * extents); packed 1D angles use the packed position (rows = N). */
+ * extents); packed 1D angles use the local packed position (rows = Nmax). */
 typedef struct pack3d_views {
   size_t rope_table, qrot, krot, vrow, kbar, vbar;
   int32_t head_dim_padded, nblk_padded, extent_table;

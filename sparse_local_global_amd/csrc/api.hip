@@ -48,7 +48,7 @@ pack3d_status check_attn(const pack3d_index* ix, const pack3d_attn* at, const ch
     return set_error(PACK3D_E_UNSUPPORTED, "%s: %d blocks per volume > %d", who, ix->nblk, kMaxBlocks);
   if (ix->bvol > kMaxBlockTokens)
     return set_error(PACK3D_E_UNSUPPORTED, "%s: %d tokens per block > %d", who, ix->bvol, kMaxBlockTokens);
-  if ((int64_t)ix->batch * at->heads * ix->tokens * padded_head_dim(at->head_dim) > ((int64_t)1 << 40))
+  if ((int64_t)ix->batch * at->heads * ix->nblk * ix->bvol * padded_head_dim(at->head_dim) > ((int64_t)1 << 40))
     return set_error(PACK3D_E_UNSUPPORTED, "%s: problem too large", who);
   return PACK3D_OK;
 }
@@ -60,7 +60,7 @@ using namespace pack3d;
 
 extern "C" const char* pack3d_last_error(void) { return g_msg; }
 
-extern "C" int32_t pack3d_version(void) { return 102; }
+extern "C" int32_t pack3d_version(void) { return 103; }
 
 extern "C" size_t pack3d_workspace_bytes(const pack3d_index* ix, const pack3d_attn* at, int for_backward) {
   if (check_attn(ix, at, "workspace_bytes") != PACK3D_OK) return 0;

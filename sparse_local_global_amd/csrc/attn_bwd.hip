@@ -6,9 +6,13 @@
 // P = exp(logit - lse) for local keys j and summaries b of query i,
 //   delta_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, V_j> - delta_i),  dT_ib = P_ib (<dO_i, Vbar_b> - delta_i)
 //   dQ~_i   = scale (sum_j dS_ij K~_j + sum_b dT_ib Kbar_b)
-//   dK~_j   = scale sum_i dS_ij Q~_i + dKbar_b(j) / |b|,  dKbar_b = scale sum_i dT_ib Q~_i
-//   dV_j    = sum_i P_ij dO_i + dVbar_b(j) / |b|,         dVbar_b = sum_i P_ib dO_i
-//   dq = R(c)^T dQ~, dk = R(c)^T dK~  (R orthogonal; the mean broadcasts 1/|b| to each member).
+//   dK~_j   = scale sum_i dS_ij Q~_i + dKbar_b(j) / n_b,  dKbar_b = scale sum_i dT_ib Q~_i
+//   dV_j    = sum_i P_ij dO_i + dVbar_b(j) / n_b,         dVbar_b = sum_i P_ib dO_i
+//   dq = R(c)^T dQ~, dk = R(c)^T dK~  (R orthogonal; the mean broadcasts 1/n_b to each of
+//   the n_b tokens present in block b, n_b = |b| on a full grid).
+// Empty canonical slots (ragged geometry) hold zero rows of Q~, K~, V and dO, and lse
+// +inf, so they add nothing to any sum; the query-major dQ kernel masks them as keys,
+// as the forward does, and no kernel writes a gradient for them.
 //
 // Kernels, in launch order (no atomics anywhere, so results are bitwise reproducible):
 //   bwd_pre      per block: delta, dO and lse (in log2 units) gathered to canonical order
@@ -42,7 +46,10 @@ struct BwdArgs {
   const void* out; const float* lse; const void* dout;
   void* dq; void* dk; void* dv;
   const int32_t* coords; const int32_t* perm; const int32_t* nbr; const int32_t* geom;
-  int B, N, H, D, Dp, nblk, nblkp, bvol, slots, radius, tiles_per_block, with_summaries, chunks;
+  const int32_t* voff; const int32_t* count; const uint32_t* occ; const uint32_t* emask;
+  // NC canonical rows per volume, Nmax the lse stride, holes: empty slots exist
+  int B, NC, Nmax, H, D, Dp, nblk, nblkp, bvol, slots, radius, tiles_per_block, with_summaries, chunks;
+  int holes, occ_words;
   int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
   int bz, by, bx;
   float scale, scale_log2;
@@ -53,6 +60,13 @@ struct alignas(sizeof(T) * V) Vec {
   T v[V];
 };
 
+// 1 / n_b of block kb of volume b: the tokens present (|b| on a full grid); 0 for an
+// empty block, whose gradients are never written.
+__device__ inline float block_inv(const BwdArgs& a, int b, int kb) {
+  const int cnt = a.holes ? a.count[(int64_t)b * a.nblk + kb] : a.bvol;
+  return cnt > 0 ? 1.0f / (float)cnt : 0.f;
+}
+
 // ---------------------------------------------------------------------------------
 // bwd_pre: one workgroup per (block, head, volume)
 // ---------------------------------------------------------------------------------
@@ -61,7 +75,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
   extern __shared__ char smem[];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int N = a.N, D = a.D, Dp = a.Dp, bvol = a.bvol;
+  const int N = a.NC, D = a.D, Dp = a.Dp, bvol = a.bvol;
   const int ntok = bvol < kTile ? bvol : kTile;
   const int nch = D / VEC;
   float* part = (float*)smem;                          // [ntok][nch] partial dot products
@@ -73,10 +87,16 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
     for (int it = tid; it < ntok * nch; it += 256) {
       const int tok = it / nch, c = (it - tok * nch) * VEC;
       const int kappa = blk * bvol + t0 + tok;
-      const int src = a.perm[(int64_t)b * N + kappa];
-      const int64_t in = (((int64_t)b * N + src) * a.H + h) * D + c;
-      const Vec<T, VEC> g = *(const Vec<T, VEC>*)(dout + in);
-      const Vec<T, VEC> o = *(const Vec<T, VEC>*)(out + in);
+      const int src = a.perm[(int64_t)b * N + kappa];   // -1: empty slot, zero row
+      Vec<T, VEC> g, o;
+      if (src >= 0) {
+        const int64_t in = (((int64_t)a.voff[b] + src) * a.H + h) * D + c;
+        g = *(const Vec<T, VEC>*)(dout + in);
+        o = *(const Vec<T, VEC>*)(out + in);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) g.v[e] = o.v[e] = (T)0.f;
+      }
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc += (float)g.v[e] * (float)o.v[e];
@@ -97,7 +117,8 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
       float s = 0.f;
       for (int c = 0; c < nch; ++c) s += part[tid * nch + c];
       a.delta[bh * N + kappa] = s;
-      a.lsec[bh * N + kappa] = a.lse[bh * N + src] * kLog2e;   // log2 units
+      // log2 units; +inf for an empty slot makes every probability of that row 0
+      a.lsec[bh * N + kappa] = src >= 0 ? a.lse[bh * a.Nmax + src] * kLog2e : INFINITY;
     }
     __syncthreads();
   }
@@ -112,12 +133,13 @@ template <typename T>
 __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, int nrows, int b, int h, int row0,
                                   bool unrotate, T* dst, int* s_src, int* s_rel) {
   const int tid = threadIdx.x;
-  const int N = a.N, D = a.D;
+  const int N = a.NC, D = a.D;
+  const int64_t tok0 = a.voff[b];
   if (tid < nrows) {
-    const int src = a.perm[(int64_t)b * N + row0 + tid];
+    const int src = a.perm[(int64_t)b * N + row0 + tid];   // -1: empty slot, not written
     s_src[tid] = src;
     const int32_t* g = a.geom + b * G_FIELDS;
-    const int32_t* c = a.coords + ((int64_t)b * N + src) * 3;
+    const int32_t* c = a.coords + (tok0 + (src >= 0 ? src : 0)) * 3;
     for (int gi = 0; gi < a.groups; ++gi) s_rel[tid * 3 + gi] = rope_row(a.pos_mode, gi, src, c, g, a.trows);
   }
   __syncthreads();
@@ -125,6 +147,7 @@ __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, in
   unrotate = unrotate && a.pos_mode != PACK3D_POS_NONE;
   for (int it = tid; it < nrows * D; it += (int)blockDim.x) {
     const int r = it / D, col = it - r * D;
+    if (s_src[r] < 0) continue;
     float v = st[r * sts + col];
     if (unrotate) {
       const int ax = col / gw, k = col - ax * gw;
@@ -133,7 +156,7 @@ __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, in
       if (k < half) v = v * cs.x + st[r * sts + col + half] * cs.y;      // y1 c + y2 s
       else v = -st[r * sts + col - half] * cs.y + v * cs.x;              // -y1 s + y2 c
     }
-    dst[(((int64_t)b * N + s_src[r]) * a.H + h) * D + col] = (T)v;
+    dst[((tok0 + s_src[r]) * a.H + h) * D + col] = (T)v;
   }
   __syncthreads();  // s_src / s_rel are rewritten by the next call
 }
@@ -161,14 +184,15 @@ void k_bwd_summary(BwdArgs a) {
   const int h = (L / nst / a.chunks) % a.H, b = L / nst / a.chunks / a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int N = a.N, bvol = a.bvol;
+  const int N = a.NC, bvol = a.bvol;
   const int64_t bh = (int64_t)b * a.H + h;
   const int sid = r0 + 16 * wave + col;          // this lane's summary (block id)
   ColFrag<T, DP> kf, vf;
   kf.load((const T*)a.kbar + (bh * a.nblkp + sid) * DP, true, grp);   // padding rows are zero
   vf.load((const T*)a.vbar + (bh * a.nblkp + sid) * DP, true, grp);
   const int32_t* g = a.geom + b * G_FIELDS;
-  const int nby = g[G_EY] / a.by, nbx = g[G_EX] / a.bx;
+  // the volume's block grid covers its bounding box: ceil(extent / b) blocks per axis
+  const int nby = (g[G_EY] + a.by - 1) / a.by, nbx = (g[G_EX] + a.bx - 1) / a.bx;
   const int sz = sid / (nby * nbx), sy = (sid / nbx) % nby, sx = sid % nbx;
   f32x4 dk[DP / 16], dv[DP / 16];
 #pragma unroll
@@ -282,10 +306,11 @@ void k_bwd_local(BwdArgs a) {
   const int kb = tile / a.tiles_per_block, ks = tile - kb * a.tiles_per_block;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int N = a.N, bvol = a.bvol;
+  const int N = a.NC, bvol = a.bvol;
   const int64_t bh = (int64_t)b * a.H + h;
   const int nk = bvol < kTile ? bvol : kTile;
   const int krow0 = kb * bvol + ks * kTile;
+  if (a.holes && !any_occupied(a.occ + (int64_t)b * a.occ_words, krow0, nk)) return;  // no key here
   const int kloc = 16 * wave + col;
   ColFrag<T, DP> kf, vf;
   kf.load((const T*)a.krot + (bh * N + krow0 + kloc) * DP, kloc < nk, grp);
@@ -359,7 +384,7 @@ void k_bwd_local(BwdArgs a) {
 
   // epilogue: dK~ = scale * acc + dKbar / |b| (then R^T), dV = acc + dVbar / |b|, each
   // staged through the same LDS rows and scattered to packed order
-  const float inv = 1.0f / (float)bvol;
+  const float inv = block_inv(a, b, kb);
   const float* dkb = a.dkbar + (bh * a.nblkp + kb) * DP;
   const float* dvb = a.dvbar + (bh * a.nblkp + kb) * DP;
 #pragma unroll
@@ -434,7 +459,7 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
   }
   __syncthreads();
   const int64_t bh = (int64_t)b * a.H + h;
-  const float inv = 1.0f / (float)a.bvol;
+  const float inv = block_inv(a, b, kb);
   f32x16(&acc)[NDT] = dk;  // the half's own tensor; filled below for qh = 1
   if (qh == 1) {
 #pragma unroll
@@ -462,12 +487,14 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
       for (int e = 0; e < 4; ++e) acc[dt][4 * jj + e] = acc[dt][4 * jj + e] * mul + sv[e] * inv;
     }
   const int row = krow0 + kloc;
-  const int src = a.perm[(int64_t)b * a.N + row];
+  const int src = a.perm[(int64_t)b * a.NC + row];
+  if (src < 0) return;  // empty slot
+  const int64_t tok0 = a.voff[b];
   // R^T on the lane's own pairs: every pair partner (+16 within an axis group, +48 for the
   // 1D rotation) keeps the dim's residue mod 8, so it sits in the same lane
   if (qh == 0 && a.pos_mode == PACK3D_POS_AXIAL) {
     const int32_t* g = a.geom + b * G_FIELDS;
-    const int32_t* c = a.coords + ((int64_t)b * a.N + src) * 3;
+    const int32_t* c = a.coords + (tok0 + src) * 3;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       int r = c[dt] - g[G_OZ + dt];
@@ -495,7 +522,7 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
         acc[(m + 6) / 4][4 * ((m + 6) % 4) + e] = -y1 * t.y + y2 * t.x;
       }
   }
-  bf16* dst = (bf16*)(qh == 0 ? a.dk : a.dv) + (((int64_t)b * a.N + src) * a.H + h) * 96;
+  bf16* dst = (bf16*)(qh == 0 ? a.dk : a.dv) + ((tok0 + src) * a.H + h) * 96;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -525,10 +552,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
-  const int N = a.N, bvol = a.bvol;
+  const int N = a.NC, bvol = a.bvol;
   const int64_t bh = (int64_t)b * a.H + h;
   const int nk = bvol < kTile ? bvol : kTile;
   const int krow0 = kb * bvol + ks * kTile;
+  if (a.holes && !any_occupied(a.occ + (int64_t)b * a.occ_words, krow0, nk)) return;  // no key here
   const int kloc = 32 * kh + col;
   ColFrag32<DP> kf, vf;
   kf.load((const bf16*)a.krot + (bh * N + krow0 + kloc) * DP, kloc < nk, half);
@@ -621,7 +649,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __syncthreads();
   // epilogue (query half 0 holds the totals): dK~ = scale * acc + dKbar / |b| (then R^T),
   // dV = acc + dVbar / |b|, each staged through LDS rows and scattered to packed order
-  const float inv = 1.0f / (float)bvol;
+  const float inv = block_inv(a, b, kb);
   const float* dkb = a.dkbar + (bh * a.nblkp + kb) * DP;
   const float* dvb = a.dvbar + (bh * a.nblkp + kb) * DP;
   if (qh == 0) {
@@ -712,10 +740,12 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
 template <typename T>
 __device__ inline void dq_epilogue96(const BwdArgs& a, f32x4 (&dq)[6], int b, int h, int row, bool ok, int grp) {
   if (!ok) return;
-  const int src = a.perm[(int64_t)b * a.N + row];
+  const int src = a.perm[(int64_t)b * a.NC + row];
+  if (src < 0) return;  // empty slot
+  const int64_t tok0 = a.voff[b];
   const int32_t* g = a.geom + b * G_FIELDS;
-  const int32_t* c = a.coords + ((int64_t)b * a.N + src) * 3;
-  T* dst = (T*)a.dq + (((int64_t)b * a.N + src) * a.H + h) * 96;
+  const int32_t* c = a.coords + (tok0 + src) * 3;
+  T* dst = (T*)a.dq + ((tok0 + src) * a.H + h) * 96;
   if (a.pos_mode == PACK3D_POS_PACKED_1D) {  // pairs (k, k + 48): dq[dt] with dq[dt + 3]
     const float2* cs = a.tab + (int64_t)src * 48 + 4 * grp;
 #pragma unroll
@@ -772,12 +802,14 @@ void k_bwd_dq(BwdArgs a) {
   const int qb = tile / a.tiles_per_block, qs = tile - qb * a.tiles_per_block;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int N = a.N, bvol = a.bvol;
+  const int N = a.NC, bvol = a.bvol;
   const int64_t bh = (int64_t)b * a.H + h;
   const int nq = bvol < kTile ? bvol : kTile;
   const int qrow0 = qb * bvol + qs * kTile;
   const int qloc = 16 * wave + col;
   const bool qok = qloc < nq;
+  const uint32_t* occ = a.occ + (int64_t)b * a.occ_words;
+  if (a.holes && !any_occupied(occ, qrow0, nq)) return;  // no token among the tile's queries
   ColFrag<T, DP> qf, gf;
   qf.load((const T*)a.qrot + (bh * N + qrow0 + qloc) * DP, qok, grp);
   gf.load((const T*)a.doc + (bh * N + qrow0 + qloc) * DP, qok, grp);
@@ -785,7 +817,8 @@ void k_bwd_dq(BwdArgs a) {
   const float delta = qok ? a.delta[bh * N + qrow0 + qloc] : 0.f;
 
   const int mask_words = a.nblkp / 32;
-  for (int i = tid; i < mask_words; i += kThreads) sm.mask[i] = 0u;
+  // summaries: empty blocks start masked (as in the forward), the local blocks are added below
+  for (int i = tid; i < mask_words; i += kThreads) sm.mask[i] = a.holes ? a.emask[(int64_t)b * mask_words + i] : 0u;
   if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
   __syncthreads();
   const int nloc = sm.nloc;
@@ -834,12 +867,14 @@ void k_bwd_dq(BwdArgs a) {
     if (t < nlt) {
       const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
       live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+      if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
     } else {
       const int ts = t - nlt, r0 = ts * kTile;
       const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
       const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
+    if (live == 0ull) return;
     dq_step(sm, qf, gf, dq, lse2, delta, c, col, grp, live);
   };
   pipeline2(total, st0, st1, fetch, store, compute);
@@ -936,7 +971,9 @@ pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3
   a.tab = (const float2*)(ws + w.rope);
   a.out = out; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
   a.coords = coords; a.perm = ix->perm; a.nbr = ix->nbr; a.geom = ix->geom;
-  a.B = d.B; a.N = d.N; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
+  a.voff = ix->voff; a.count = ix->count; a.occ = ix->occ; a.emask = ix->emask;
+  a.holes = d.holes; a.occ_words = ix->occ_words;
+  a.B = d.B; a.NC = d.NC; a.Nmax = d.Nmax; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.slots = d.slots; a.radius = ix->radius;
   a.tiles_per_block = d.bvol > kTile ? d.bvol / kTile : 1;
   a.with_summaries = at->with_summaries ? 1 : 0;

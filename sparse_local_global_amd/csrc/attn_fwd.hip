@@ -29,11 +29,14 @@
 namespace pack3d {
 namespace {
 
+// NC canonical rows per volume; Nmax: lse stride; holes: canonical slots may be empty
+// (occ: bit per slot, emask: bit per empty block), else both are unused.
 struct FwdArgs {
   const void* qrot; const void* krot; const void* vr; const void* kbar; const void* vbar;
-  const int32_t* perm; const int32_t* nbr;
+  const int32_t* perm; const int32_t* nbr; const int32_t* voff;
+  const uint32_t* occ; const uint32_t* emask;
   void* out; float* lse;
-  int N, H, D, nblk, nblkp, bvol, slots, tiles_per_block, with_summaries;
+  int NC, Nmax, H, D, nblk, nblkp, bvol, slots, tiles_per_block, with_summaries, holes, occ_words;
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -85,7 +88,7 @@ __device__ inline void tile_step(const FwdSmem<T, DP>& sm, const ColFrag<T, DP>&
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   mx *= c;  // scale > 0: the maximum of the scaled logits
   if (mx > st.m + kRescale) {
-    // every query's first tile holds keys of its own block, so mx is finite here
+    // tiles without a live row are skipped, so mx is finite here
     const float alpha = fast_exp2(st.m - mx);
     st.m = mx;
     st.l *= alpha;
@@ -118,14 +121,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int qb = tile / a.tiles_per_block, qsub = tile - qb * a.tiles_per_block;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int N = a.N, bvol = a.bvol;
+  const int N = a.NC, bvol = a.bvol;
   const int64_t bh = (int64_t)b * a.H + h;
   const int nq = bvol < kTile ? bvol : kTile;
   const int qrow0 = qb * bvol + qsub * kTile;
   const int mask_words = a.nblkp / 32;
+  const uint32_t* occ = a.occ + (int64_t)b * a.occ_words;
+  if (a.holes && !any_occupied(occ, qrow0, nq)) return;  // no token among the tile's queries
 
-  // compacted neighbour list (wave 0) and the summary bitmask of the local blocks
-  for (int i = tid; i < mask_words; i += kThreads) sm.mask[i] = 0u;
+  // compacted neighbour list (wave 0) and the summary bitmask: empty blocks start
+  // masked, the local blocks are added below
+  for (int i = tid; i < mask_words; i += kThreads) sm.mask[i] = a.holes ? a.emask[(int64_t)b * mask_words + i] : 0u;
   if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
   __syncthreads();
   const int nloc = sm.nloc;
@@ -186,12 +192,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (t < nlt) {
       const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
       live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+      if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
     } else {
       const int ts = t - nlt, r0 = ts * kTile;
       const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
       const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
+    if (live == 0ull) return;  // all masked (empty slots): nothing to add, and m may still be -inf
     tile_step(sm, f, st, c, col, grp, live);
   };
   pipeline2(total, st0, st1, fetch, store, compute);
@@ -200,10 +208,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (qloc < nq) {
-    const int src = a.perm[(int64_t)b * N + qrow0 + qloc];
+  const int src = qloc < nq ? a.perm[(int64_t)b * N + qrow0 + qloc] : -1;  // -1: empty slot
+  if (src >= 0) {
     const float inv = 1.0f / l;
-    T* orow = (T*)a.out + (((int64_t)b * N + src) * a.H + h) * a.D;
+    T* orow = (T*)a.out + (((int64_t)a.voff[b] + src) * a.H + h) * a.D;
 #pragma unroll
     for (int dt = 0; dt < DP / 16; ++dt) {
 #pragma unroll
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (d < a.D) orow[d] = (T)(st.o[dt][i] * inv);
       }
     }
-    if (grp == 0) a.lse[bh * N + src] = st.m * kLn2 + logf(l);
+    if (grp == 0) a.lse[bh * a.Nmax + src] = st.m * kLn2 + logf(l);
   }
 }
 
@@ -284,13 +292,15 @@ __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2)))
   const int qb = tile / a.tiles_per_block, qsub = tile - qb * a.tiles_per_block;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int N = a.N, bvol = a.bvol;
+  const int N = a.NC, bvol = a.bvol;
   const int64_t bh = (int64_t)b * a.H + h;
   const int nq = bvol < kTile ? bvol : kTile;
   const int qrow0 = qb * bvol + qsub * kTile;
   const int mask_words = a.nblkp / 32;
+  const uint32_t* occ = a.occ + (int64_t)b * a.occ_words;
+  if (a.holes && !any_occupied(occ, qrow0, nq)) return;  // no token among the tile's queries
 
-  for (int i = tid; i < mask_words; i += kThreads32) sm.mask[i] = 0u;
+  for (int i = tid; i < mask_words; i += kThreads32) sm.mask[i] = a.holes ? a.emask[(int64_t)b * mask_words + i] : 0u;
   if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
   __syncthreads();
   const int nloc = sm.nloc;
@@ -347,22 +357,24 @@ __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2)))
     if (t < nlt) {
       const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
       live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+      if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
     } else {
       const int ts = t - nlt, r0 = ts * kTile;
       const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
       const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
+    if (live == 0ull) return;
     tile_step32(sm, f, st, c, lane, half, live);
   };
   pipeline1(total, st0, fetch, store, compute);
 
   // epilogue: o = acc / l, lse = m ln2 + ln l, scattered back to packed order
   float l = st.l + __shfl_xor(st.l, 32);
-  if (qloc < nq) {
-    const int src = a.perm[(int64_t)b * N + qrow0 + qloc];
+  const int src = qloc < nq ? a.perm[(int64_t)b * N + qrow0 + qloc] : -1;  // -1: empty slot
+  if (src >= 0) {
     const float inv = 1.0f / l;
-    bf16* orow = (bf16*)a.out + (((int64_t)b * N + src) * a.H + h) * a.D;
+    bf16* orow = (bf16*)a.out + (((int64_t)a.voff[b] + src) * a.H + h) * a.D;
     if (a.D == DP) {
       // slots 4j .. 4j+3 are consecutive dims: 8-byte stores
 #pragma unroll
@@ -382,7 +394,7 @@ __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2)))
         }
       }
     }
-    if (half == 0) a.lse[bh * N + src] = st.m * kLn2 + logf(l);
+    if (half == 0) a.lse[bh * a.Nmax + src] = st.m * kLn2 + logf(l);
   }
 }
 
@@ -418,8 +430,9 @@ pack3d_status launch_attn_fwd(const Dims& d, const pack3d_index* ix, const pack3
                               const char* ws, const Workspace& w, void* out, float* lse, hipStream_t s) {
   FwdArgs a;
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
-  a.perm = ix->perm; a.nbr = ix->nbr; a.out = out; a.lse = lse;
-  a.N = d.N; a.H = d.H; a.D = d.D; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol; a.slots = d.slots;
+  a.perm = ix->perm; a.nbr = ix->nbr; a.voff = ix->voff; a.occ = ix->occ; a.emask = ix->emask;
+  a.out = out; a.lse = lse;
+  a.NC = d.NC; a.Nmax = d.Nmax; a.holes = d.holes; a.occ_words = ix->occ_words; a.H = d.H; a.D = d.D; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol; a.slots = d.slots;
   a.tiles_per_block = d.bvol > kTile ? d.bvol / kTile : 1;
   a.with_summaries = at->with_summaries ? 1 : 0;
   const float scale = at->softmax_scale > 0.f ? at->softmax_scale : 1.0f / std::sqrt((float)d.D);

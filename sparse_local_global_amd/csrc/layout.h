@@ -13,7 +13,9 @@ constexpr int kTile = 64;             // query rows / key rows per tile
 inline int padded_head_dim(int d) { return (d + 31) / 32 * 32; }
 
 struct Dims {
-  int B, N, H, D, Dp, nblk, nblkp, bvol, slots, emax;
+  // NC: canonical rows per volume (nblk * bvol); Nmax: tokens of the largest volume (the
+  // lse stride); holes: some canonical slot is empty
+  int B, NC, Nmax, H, D, Dp, nblk, nblkp, bvol, slots, emax, holes;
   // rotation: `groups` contiguous head-dim groups of width gw, `half` = gw / 2 pairs
   // (k, k + half) each, table of `trows` angle rows (positions) x half
   int pos_mode, groups, gw, half, trows;
@@ -22,7 +24,8 @@ struct Dims {
 
 inline Dims make_dims(const pack3d_index* ix, const pack3d_attn* at) {
   Dims d;
-  d.B = ix->batch; d.N = ix->tokens; d.H = at->heads; d.D = at->head_dim;
+  d.B = ix->batch; d.NC = ix->nblk * ix->bvol; d.Nmax = ix->tokens; d.H = at->heads; d.D = at->head_dim;
+  d.holes = ix->holes;
   d.Dp = padded_head_dim(at->head_dim);
   d.nblk = ix->nblk; d.nblkp = (ix->nblk + kTile - 1) / kTile * kTile;
   d.bvol = ix->bvol; d.slots = ix->slots;
@@ -33,7 +36,7 @@ inline Dims make_dims(const pack3d_index* ix, const pack3d_attn* at) {
   d.groups = d.pos_mode == PACK3D_POS_AXIAL ? 3 : 1;
   d.gw = d.D / d.groups;
   d.half = d.gw / 2;
-  d.trows = d.pos_mode == PACK3D_POS_AXIAL ? d.emax : (d.pos_mode == PACK3D_POS_PACKED_1D ? d.N : 1);
+  d.trows = d.pos_mode == PACK3D_POS_AXIAL ? d.emax : (d.pos_mode == PACK3D_POS_PACKED_1D ? d.Nmax : 1);
   d.esize = at->dtype == PACK3D_BF16 ? 2 : 4;
   return d;
 }
@@ -57,7 +60,7 @@ struct Workspace {
 inline Workspace workspace_layout(const Dims& d) {
   Workspace w;
   const size_t bh = (size_t)d.B * d.H;
-  const size_t act = bh * d.N * d.Dp * d.esize;
+  const size_t act = bh * d.NC * d.Dp * d.esize;
   const size_t summ = bh * d.nblkp * d.Dp * d.esize;
   const size_t summ32 = bh * d.nblkp * d.Dp * sizeof(float);
   size_t off = 0;
@@ -70,8 +73,8 @@ inline Workspace workspace_layout(const Dims& d) {
   w.vbar = take(summ);
   w.fwd_total = off;
   w.doc = take(act);
-  w.lsec = take(sizeof(float) * bh * d.N);
-  w.delta = take(sizeof(float) * bh * d.N);
+  w.lsec = take(sizeof(float) * bh * d.NC);
+  w.delta = take(sizeof(float) * bh * d.NC);
   w.dkbar = take(summ32);
   w.dvbar = take(summ32);
   w.part_k = take(summ32 * summary_chunks(d));

@@ -13,10 +13,11 @@
 //
 // One workgroup per (block, head group, volume).  The block's tokens are gathered
 // from packed order (perm); Q and K are rotated in fp32 and written with V in
-// canonical order [B, H, N, Dp] (rows zero-padded to Dp); the block means of the
-// rotated K and of V ([B, H, nblkp, Dp], zero padding rows) are summed in a fixed
-// order from LDS, so results are bitwise reproducible and independent of the
-// packing.  HBM bound: reads q, k, v once, writes the rotated Q, K and V once.
+// canonical order [B, H, NC, Dp] (rows zero-padded to Dp, empty slots zero rows);
+// the block means of the rotated K and of V over the tokens present ([B, H, nblkp,
+// Dp], zero rows for empty and padding blocks) are summed in a fixed order from
+// LDS, so results are bitwise reproducible and independent of the packing.  HBM
+// bound: reads q, k, v once, writes the rotated Q, K and V once.
 #include <cmath>
 
 #include "layout.h"
@@ -47,10 +48,10 @@ __device__ inline T from_f(float x) { return (T)x; }
 
 struct RopeArgs {
   const void* q; const void* k; const void* v;
-  const int32_t* coords; const int32_t* perm; const int32_t* geom;
+  const int32_t* coords; const int32_t* perm; const int32_t* geom; const int32_t* voff; const int32_t* count;
   const float2* tab;
   void* qrot; void* krot; void* vr; void* kbar; void* vbar;
-  int N, H, D, Dp, nblk, nblkp, bvol, heads_per_group;
+  int NC, H, D, Dp, nblk, nblkp, bvol, heads_per_group, holes;
   int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
 };
 
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   extern __shared__ char smem[];
   const int blk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int N = a.N, H = a.H, D = a.D, Dp = a.Dp, bvol = a.bvol;
+  const int NC = a.NC, H = a.H, D = a.D, Dp = a.Dp, bvol = a.bvol;
   const int gw = D / GROUPS, half = gw / 2;
   constexpr int groups = GROUPS;
   const int ntok = bvol < kChunk ? bvol : kChunk;
@@ -73,12 +74,17 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   float* vl = kl + ntok * ls;
 
   const int32_t* g = a.geom + b * G_FIELDS;
+  const int64_t tok0 = a.voff[b];  // packed token offset of the volume
   for (int t = tid; t < bvol; t += 256) {
     const int kappa = blk * bvol + t;
-    const int src = a.perm[(int64_t)b * N + kappa];
+    const int src = a.perm[(int64_t)b * NC + kappa];  // -1: empty slot
     s_src[t] = src;
-    const int32_t* c = a.coords + ((int64_t)b * N + src) * 3;
-    for (int gi = 0; gi < GROUPS; ++gi) s_rel[t * 3 + gi] = rope_row(a.pos_mode, gi, src, c, g, a.trows);
+    if (src >= 0) {
+      const int32_t* c = a.coords + (tok0 + src) * 3;
+      for (int gi = 0; gi < GROUPS; ++gi) s_rel[t * 3 + gi] = rope_row(a.pos_mode, gi, src, c, g, a.trows);
+    } else {
+      for (int gi = 0; gi < GROUPS; ++gi) s_rel[t * 3 + gi] = 0;
+    }
   }
   __syncthreads();
 
@@ -107,11 +113,17 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         const int src = s_src[t0 + tok];
         const int c = s_rel[(t0 + tok) * 3 + ax];
         const int col1 = ax * gw + p * VEC, col2 = col1 + half;
-        const int64_t in_row = ((int64_t)b * N + src) * H + h;
-        const Vec<T, VEC> q1 = *(const Vec<T, VEC>*)(q + in_row * D + col1);
-        const Vec<T, VEC> q2 = *(const Vec<T, VEC>*)(q + in_row * D + col2);
-        const Vec<T, VEC> k1 = *(const Vec<T, VEC>*)(k + in_row * D + col1);
-        const Vec<T, VEC> k2 = *(const Vec<T, VEC>*)(k + in_row * D + col2);
+        Vec<T, VEC> q1, q2, k1, k2;
+        if (src >= 0) {
+          const int64_t in_row = (tok0 + src) * H + h;
+          q1 = *(const Vec<T, VEC>*)(q + in_row * D + col1);
+          q2 = *(const Vec<T, VEC>*)(q + in_row * D + col2);
+          k1 = *(const Vec<T, VEC>*)(k + in_row * D + col1);
+          k2 = *(const Vec<T, VEC>*)(k + in_row * D + col2);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) q1.v[e] = q2.v[e] = k1.v[e] = k2.v[e] = from_f<T>(0.f);
+        }
         Vec<T, VEC> oq1, oq2, ok1, ok2;
         const float2* cs = a.tab + (int64_t)c * half + p * VEC;
 #pragma unroll
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           kl[tok * ls + col1 + e] = ky1;
           kl[tok * ls + col2 + e] = ky2;
         }
-        const int64_t out_row = (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp;
+        const int64_t out_row = (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp;
         *(Vec<T, VEC>*)(qrot + out_row + col1) = oq1;
         *(Vec<T, VEC>*)(qrot + out_row + col2) = oq2;
         *(Vec<T, VEC>*)(krot + out_row + col1) = ok1;
@@ -140,8 +152,14 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         const int tok = it / (D / VEC);
         const int col = (it - tok * (D / VEC)) * VEC;
         const int src = s_src[t0 + tok];
-        const Vec<T, VEC> x = *(const Vec<T, VEC>*)(v + (((int64_t)b * N + src) * H + h) * D + col);
-        *(Vec<T, VEC>*)(vr + (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp + col) = x;
+        Vec<T, VEC> x;
+        if (src >= 0) {
+          x = *(const Vec<T, VEC>*)(v + ((tok0 + src) * H + h) * D + col);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x.v[e] = from_f<T>(0.f);
+        }
+        *(Vec<T, VEC>*)(vr + (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp + col) = x;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) vl[tok * ls + col + e] = to_f(x.v[e]);
       }
@@ -150,7 +168,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         const int pad = Dp - D;
         for (int it = tid; it < ntok * pad; it += 256) {
           const int tok = it / pad, col = D + it - tok * pad;
-          const int64_t out_row = (bh * N + (int64_t)blk * bvol + t0 + tok) * Dp;
+          const int64_t out_row = (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp;
           qrot[out_row + col] = from_f<T>(0.f);
           krot[out_row + col] = from_f<T>(0.f);
           vr[out_row + col] = from_f<T>(0.f);
@@ -171,7 +189,9 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
       __syncthreads();
     }
     if (tid < Dp) {
-      const float inv = 1.0f / (float)bvol;
+      // mean over the tokens present (|b| on a full grid); an empty block's sums are 0
+      const int cnt = a.holes ? a.count[(int64_t)b * a.nblk + blk] : bvol;
+      const float inv = cnt > 0 ? 1.0f / (float)cnt : 0.f;
       ((T*)a.kbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(ksum * inv);
       ((T*)a.vbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(vsum * inv);
       // zero the padding summaries nblk .. nblkp (there may be more of them than blocks)
@@ -223,9 +243,10 @@ pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack
   }
   RopeArgs a;
   a.q = q; a.k = k; a.v = v; a.coords = coords; a.perm = ix->perm; a.geom = ix->geom;
+  a.voff = ix->voff; a.count = ix->count; a.holes = d.holes;
   a.tab = (const float2*)(ws + w.rope);
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
-  a.N = d.N; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
+  a.NC = d.NC; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.pos_mode = d.pos_mode; a.groups = d.groups; a.gw = d.gw; a.half = d.half; a.trows = d.trows;
   // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all
   int hp = d.H;

@@ -532,6 +532,26 @@ struct VirtualRows {
   }
 };
 
+// Bit r set: tile row r is a canonical slot that holds a token (occ: one bit per slot of
+// the volume).  Lane r tests row r; every lane of the wave must call it.
+__device__ inline uint64_t occupied_rows(const uint32_t* __restrict__ occ, const VirtualRows& vr, int valid) {
+  const int lane = threadIdx.x & 63;
+  bool p = false;
+  if (lane < valid) {
+    const int row = vr.row(lane);
+    p = (occ[row >> 5] >> (row & 31)) & 1u;
+  }
+  return __ballot(p);
+}
+
+// Whether any of the n canonical rows from row0 holds a token.
+__device__ inline bool any_occupied(const uint32_t* __restrict__ occ, int row0, int n) {
+  const int lane = threadIdx.x & 63;
+  bool p = false;
+  for (int r = lane; r < n; r += 64) p |= (occ[(row0 + r) >> 5] >> ((row0 + r) & 31)) & 1u;
+  return __ballot(p) != 0ull;
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin by linear id.  Map linear id L to a
 // logical tile so that each XCD walks a contiguous range of logical tiles: neighbouring
 // tiles share their key / value tiles, which then stay in that XCD's L2.

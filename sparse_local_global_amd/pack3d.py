@@ -28,7 +28,9 @@ class Pack3DError(RuntimeError):
 
 
 class Packing(ctypes.Structure):
-    _fields_ = [("batch", ctypes.c_int32), ("tokens_per_volume", ctypes.c_int32), ("order_hint", ctypes.c_int32)]
+    _fields_ = [("batch", ctypes.c_int32), ("tokens_per_volume", ctypes.c_int32), ("order_hint", ctypes.c_int32),
+                ("ragged", ctypes.c_int32), ("volume_offsets", ctypes.POINTER(ctypes.c_int32)),
+                ("max_blocks", ctypes.c_int32)]
 
 
 class Attn(ctypes.Structure):
@@ -42,7 +44,12 @@ class Tables(ctypes.Structure):
                 ("nbr", ctypes.c_void_p), ("geom", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("tokens", ctypes.c_int32), ("nblk", ctypes.c_int32),
                 ("block_tokens", ctypes.c_int32), ("slots", ctypes.c_int32), ("radius", ctypes.c_int32),
-                ("block_shape", ctypes.c_int32 * 3), ("extent_max", ctypes.c_int32 * 3)]
+                ("block_shape", ctypes.c_int32 * 3), ("extent_max", ctypes.c_int32 * 3),
+                ("block_count", ctypes.c_void_p), ("volume_offsets", ctypes.c_void_p),
+                ("total_tokens", ctypes.c_int64), ("ragged", ctypes.c_int32), ("holes", ctypes.c_int32)]
+
+
+GEOM_FIELDS = 10
 
 
 class Views(ctypes.Structure):
@@ -57,6 +64,9 @@ EXPORTS = {
     "pack3d_build_index": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Packing), ctypes.POINTER(ctypes.c_int32),
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                           ctypes.POINTER(ctypes.c_void_p)]),
+    "pack3d_measure_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Packing), ctypes.POINTER(ctypes.c_int32),
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                             ctypes.POINTER(ctypes.c_int32)]),
     "pack3d_index_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Tables)]),
     "pack3d_index_geometry": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "pack3d_index_free": (None, [ctypes.c_void_p]),
@@ -106,13 +116,24 @@ def _ptr(t):
 
 
 class Index:
-    """A built PACK3D index: the device tables (owned here) plus the library handle."""
+    """A built PACK3D index: the device tables (owned here) plus the library handle.
 
-    def __init__(self, handle, tables: torch.Tensor, batch, tokens, block_shape, radius):
+    ``offsets`` is None for the uniform layout ([B, N, ...] tensors) or the B + 1 token
+    offsets of a varlen batch (flat [T, ...] tensors); ``tokens`` is the largest volume."""
+
+    def __init__(self, handle, tables: torch.Tensor, batch, tokens, block_shape, radius, offsets=None,
+                 ragged=False):
         self._handle = handle
         self.tables_buffer = tables
         self.batch, self.tokens = batch, tokens
         self.block_shape, self.radius = tuple(block_shape), radius
+        self.offsets = None if offsets is None else [int(o) for o in offsets]
+        self.total = batch * tokens if offsets is None else self.offsets[-1]
+        self.ragged = ragged
+
+    def act_shape(self, h, d):
+        """Shape of q, k, v, out and the gradients for this layout."""
+        return (self.batch, self.tokens, h, d) if self.offsets is None else (self.total, h, d)
 
     @property
     def handle(self):
@@ -137,16 +158,22 @@ class Index:
         return self.tables_buffer[off: off + 4 * count].view(torch.int32)
 
     def tables(self) -> dict:
+        """Device views: token_block, canon [B, N] (uniform) or [T] (varlen); perm [B, nblk |b|]
+        (-1 = empty slot); nbr [B, nblk, slots]; block_count [B, nblk]; geom [B, 10]."""
         t = Tables()
         _check(load_library().pack3d_index_tables(self.handle, ctypes.byref(t)))
-        b, n, nblk, slots = t.batch, t.tokens, t.nblk, t.slots
-        return dict(token_block=self._view(t.token_block, b * n).view(b, n),
-                    canon=self._view(t.canon, b * n).view(b, n),
-                    perm=self._view(t.perm, b * n).view(b, n),
+        b, nblk, slots, total = t.batch, t.nblk, t.slots, t.total_tokens
+        tok_shape = (b, t.tokens) if self.offsets is None else (total,)
+        nc = nblk * t.block_tokens
+        return dict(token_block=self._view(t.token_block, total).view(*tok_shape),
+                    canon=self._view(t.canon, total).view(*tok_shape),
+                    perm=self._view(t.perm, b * nc).view(b, nc),
                     nbr=self._view(t.nbr, b * nblk * slots).view(b, nblk, slots),
-                    geom=self._view(t.geom, b * 8).view(b, 8),
+                    block_count=self._view(t.block_count, b * nblk).view(b, nblk),
+                    volume_offsets=self._view(t.volume_offsets, b + 1),
+                    geom=self._view(t.geom, b * GEOM_FIELDS).view(b, GEOM_FIELDS),
                     nblk=nblk, block_tokens=t.block_tokens, slots=slots,
-                    extent_max=tuple(t.extent_max))
+                    extent_max=tuple(t.extent_max), ragged=bool(t.ragged), holes=bool(t.holes))
 
     def geometry(self, volume: int):
         out = (ctypes.c_int32 * 6)()
@@ -154,27 +181,69 @@ class Index:
         return tuple(out[:3]), tuple(out[3:])
 
 
-def index_bytes(batch, tokens, block_shape, radius) -> int:
-    p = Packing(batch, tokens, 0)
+def _packing(batch, tokens, order_hint="any", ragged=False, offsets=None, max_blocks=0):
+    """Packing struct; the offsets array is kept alive on the struct."""
+    p = Packing(batch, tokens, ORDERS.get(order_hint, 0), 1 if ragged else 0, None, max_blocks)
+    if offsets is not None:
+        arr = (ctypes.c_int32 * len(offsets))(*[int(o) for o in offsets])
+        p.volume_offsets = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+        p._keep = arr
+    return p
+
+
+def index_bytes(batch, tokens, block_shape, radius, *, ragged=False, offsets=None, max_blocks=0) -> int:
+    p = _packing(batch, tokens, ragged=ragged, offsets=offsets, max_blocks=max_blocks)
     bs = (ctypes.c_int32 * 3)(*block_shape)
     return load_library().pack3d_index_bytes(ctypes.byref(p), bs, radius)
 
 
-def build_index(coords: torch.Tensor, block_shape, local_radius: int, order_hint: str = "any") -> Index:
-    """coords: int32 [B, N, 3] (z, y, x) on the GPU."""
+def measure_blocks(coords: torch.Tensor, block_shape, *, offsets=None) -> int:
+    """Blocks per volume (the largest) that ragged coordinates need (synchronizes)."""
     lib = load_library()
-    if coords.dtype != torch.int32 or coords.dim() != 3 or coords.shape[-1] != 3 or not coords.is_cuda:
-        raise Pack3DError(E_INVALID, "coords must be a CUDA int32 tensor [B, N, 3]")
+    b, n = _coords_layout(coords, offsets)
+    p = _packing(b, n, ragged=True, offsets=offsets)
+    bs = (ctypes.c_int32 * 3)(*block_shape)
+    scratch = torch.empty(64 * b, dtype=torch.uint8, device=coords.device)
+    out = ctypes.c_int32()
+    _check(lib.pack3d_measure_blocks(_ptr(coords.contiguous()), ctypes.byref(p), bs, _ptr(scratch), scratch.numel(),
+                                     ctypes.c_void_p(_stream()), ctypes.byref(out)))
+    return out.value
+
+
+def _coords_layout(coords, offsets):
+    """(batch, tokens per volume or 0) of coords [B, N, 3] or flat [T, 3] with offsets."""
+    if coords.dtype != torch.int32 or coords.shape[-1] != 3 or not coords.is_cuda:
+        raise Pack3DError(E_INVALID, "coords must be a CUDA int32 tensor [B, N, 3] or [T, 3]")
+    if offsets is None:
+        if coords.dim() != 3:
+            raise Pack3DError(E_INVALID, "coords must be [B, N, 3] without offsets")
+        return coords.shape[0], coords.shape[1]
+    if coords.dim() != 2 or int(offsets[-1]) != coords.shape[0]:
+        raise Pack3DError(E_INVALID, "with offsets, coords must be [T, 3] with T = offsets[-1]")
+    return len(offsets) - 1, 0
+
+
+def build_index(coords: torch.Tensor, block_shape, local_radius: int, order_hint: str = "any", *,
+                ragged: bool = False, offsets=None) -> Index:
+    """coords: int32 [B, N, 3] (z, y, x) on the GPU, or flat [T, 3] with ``offsets`` (B + 1 host
+    ints) for volumes of different token counts.  ``ragged``: any set of distinct points
+    (partial edge blocks, holes); otherwise every volume must be a full grid divisible by the
+    block."""
+    lib = load_library()
+    b, n = _coords_layout(coords, offsets)
     coords = coords.contiguous()
-    b, n = coords.shape[0], coords.shape[1]
-    p = Packing(b, n, ORDERS.get(order_hint, 0))
+    max_blocks = measure_blocks(coords, block_shape, offsets=offsets) if ragged else 0
+    p = _packing(b, n, order_hint, ragged, offsets, max_blocks)
     bs = (ctypes.c_int32 * 3)(*block_shape)
     nbytes = lib.pack3d_index_bytes(ctypes.byref(p), bs, local_radius)
-    tables = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=coords.device)
+    if nbytes == 0:
+        raise Pack3DError(E_INVALID, "invalid batch layout, block shape or radius")
+    tables = torch.empty(nbytes, dtype=torch.uint8, device=coords.device)
     handle = ctypes.c_void_p()
     _check(lib.pack3d_build_index(_ptr(coords), ctypes.byref(p), bs, local_radius, _ptr(tables),
                                   nbytes, ctypes.c_void_p(_stream()), ctypes.byref(handle)))
-    return Index(handle, tables, b, n, block_shape, local_radius)
+    nmax = n if offsets is None else max(int(offsets[i + 1]) - int(offsets[i]) for i in range(b))
+    return Index(handle, tables, b, nmax, block_shape, local_radius, offsets, ragged)
 
 
 POSITION_MODES = {"axial": 0, "packed1d": 1, "none": 2}
@@ -203,12 +272,14 @@ def _check_act(name, t, shape, dtype):
 
 def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, with_summaries=True,
             workspace: torch.Tensor | None = None, out=None, lse=None, position_mode="axial"):
-    """PACK3D forward.  q, k, v [B, N, H, D]; returns (out [B, N, H, D], lse fp32 [B, H, N])."""
+    """PACK3D forward.  q, k, v [B, N, H, D] (or [T, H, D] for a varlen index); returns (out
+    shaped like q, lse fp32 [B, H, Nmax])."""
     lib = load_library()
-    b, n, h, d = q.shape
+    h, d = q.shape[-2], q.shape[-1]
+    b, n = index.batch, index.tokens
     attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries, position_mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_act(name, t, (b, n, h, d), q.dtype)
+        _check_act(name, t, index.act_shape(h, d), q.dtype)
     need = workspace_bytes(index, attn)
     if need == 0:
         raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
@@ -233,10 +304,12 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
     with workspace_bytes(..., for_backward=True)) and still holds its intermediates, so the
     backward skips recomputing them."""
     lib = load_library()
-    b, n, h, d = q.shape
+    h, d = q.shape[-2], q.shape[-1]
     attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries, position_mode)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        _check_act(name, t, (b, n, h, d), q.dtype)
+        _check_act(name, t, index.act_shape(h, d), q.dtype)
+    if tuple(lse.shape) != (index.batch, h, index.tokens):
+        raise Pack3DError(E_INVALID, f"lse must be [{index.batch}, {h}, {index.tokens}]")
     need = workspace_bytes(index, attn, True)
     if need == 0:
         raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
@@ -254,11 +327,15 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
 
 def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_base=10000.0,
                     position_mode="axial") -> dict:
-    """Tensor views of the forward intermediates left in ``workspace``."""
-    b, n, h, d = q_shape
+    """Tensor views of the forward intermediates left in ``workspace`` (canonical rows:
+    nblk * |b| per volume)."""
+    h, d = q_shape[-2], q_shape[-1]
+    b = index.batch
     attn = make_attn(dtype, h, d, rope_base, position_mode=position_mode)
     vw = Views()
     _check(load_library().pack3d_workspace_views(index.handle, ctypes.byref(attn), ctypes.byref(vw)))
+    t = index.tables()
+    n = t["nblk"] * t["block_tokens"]
     dp, nbp = vw.head_dim_padded, vw.nblk_padded
     es = 2 if dtype == torch.bfloat16 else 4
 
@@ -306,7 +383,7 @@ class Pack3DAttention(torch.autograd.Function):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         # the workspace is sized for the backward and kept, so the backward reuses the
         # forward's rotated and pooled operands instead of recomputing them
-        attn = make_attn(q.dtype, q.shape[2], q.shape[3], rope_base, scale, with_summaries, position_mode)
+        attn = make_attn(q.dtype, q.shape[-2], q.shape[-1], rope_base, scale, with_summaries, position_mode)
         need = workspace_bytes(index, attn, True)
         if need == 0:
             raise Pack3DError(E_UNSUPPORTED, load_library().pack3d_last_error().decode())

@@ -199,3 +199,13 @@ def make_ragged_inputs(grids, heads, head_dim, dtype=torch.float32, *, occupancy
     if with_grad:
         out["do"] = torch.cat(dos).contiguous()
     return out
+
+
+# Ragged stand-ins for cropped, partly occupied microscopy volumes: two volumes of
+# different shapes (extents not divisible by the block) with random holes, flat in a
+# varlen batch; about 111k tokens in all, sized like the 65k-per-volume workload.
+RAGGED_WORKLOADS = {
+    "65k-ragged": dict(grids=[(30, 34, 62), (32, 30, 60)], occupancy=0.92, block=(4, 4, 4), radius=1, heads=8,
+                       head_dim=96, seed=5, description="2 volumes 30x34x62 and 32x30x60 at 92% occupancy "
+                       "(varlen, partial edge blocks, holes), 8 heads, D=96, 4x4x4 blocks"),
+}

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     lib = p3.load_library()
     names = _declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) <= set(p3.EXPORTS)
@@ -40,7 +40,7 @@ def test_exported_symbols_in_dynamic_table():
 
 def test_version_and_last_error():
     lib = p3.load_library()
-    assert lib.pack3d_version() == 102
+    assert lib.pack3d_version() == 103
     assert isinstance(lib.pack3d_last_error(), bytes)
 
 
@@ -48,7 +48,9 @@ def test_index_bytes_depends_only_on_layout():
     assert p3.index_bytes(2, 65536, (4, 4, 4), 1) > 0
     nblk, slots = 1024, 27
     expect = 0
-    for count in (2 * 8, 2 * 65536, 2 * 65536, 2 * 65536, 2 * nblk * slots):
+    # geom, offsets, token_block, canon, perm, nbr, block counts, occupancy bits, empty-block bits
+    for count in (2 * 10, 3, 2 * 65536, 2 * 65536, 2 * 65536, 2 * nblk * slots, 2 * nblk, 2 * 65536 // 32,
+                  2 * nblk // 32):
         expect = (expect + 4 * count + 255) // 256 * 256
     assert p3.index_bytes(2, 65536, (4, 4, 4), 1) == expect
     assert p3.index_bytes(1, 100, (4, 4, 4), 1) == 0      # 100 tokens cannot tile into 64-token blocks
@@ -102,3 +104,44 @@ def test_position_mode_argument():
     with pytest.raises(p3.Pack3DError) as e:
         p3.make_attn(torch.float32, 2, 12, position_mode="sequence")
     assert e.value.status == p3.E_INVALID
+
+
+def test_ragged_and_varlen_index_bytes():
+    full = p3.index_bytes(2, 65536, (4, 4, 4), 1)
+    # varlen offsets describing the same two volumes size the same tables
+    assert p3.index_bytes(2, 0, (4, 4, 4), 1, offsets=[0, 65536, 131072]) == full
+    # ragged: sized by max_blocks, not by the token counts
+    assert p3.index_bytes(2, 65536, (4, 4, 4), 1, ragged=True, max_blocks=1024) == full
+    assert p3.index_bytes(2, 65536, (4, 4, 4), 1, ragged=True, max_blocks=2048) > full
+    assert p3.index_bytes(1, 100, (4, 4, 4), 1, ragged=True, max_blocks=4) > 0   # any token count
+    assert p3.index_bytes(1, 100, (4, 4, 4), 1, ragged=True) == 0                # needs max_blocks
+    assert p3.index_bytes(2, 0, (2, 2, 2), 1, offsets=[0, 64, 40]) == 0          # decreasing offsets
+    assert p3.index_bytes(2, 0, (2, 2, 2), 1, offsets=[0, 64, 64]) == 0          # empty volume
+    assert p3.index_bytes(2, 0, (2, 2, 2), 1, offsets=[8, 64, 72]) == 0          # must start at 0
+    assert p3.index_bytes(2, 0, (4, 4, 4), 1, offsets=[0, 64, 100]) == 0         # 36 tokens without ragged
+
+
+def test_measure_blocks_argument_errors():
+    lib = p3.load_library()
+    pk = p3._packing(1, 512, ragged=True)
+    bs = (ctypes.c_int32 * 3)(2, 2, 2)
+    out = ctypes.c_int32()
+    st = lib.pack3d_measure_blocks(None, ctypes.byref(pk), bs, ctypes.c_void_p(256), 64, None, ctypes.byref(out))
+    assert st == p3.E_INVALID
+    st = lib.pack3d_measure_blocks(ctypes.c_void_p(256), ctypes.byref(pk), bs, ctypes.c_void_p(256), 8, None,
+                                   ctypes.byref(out))
+    assert st == p3.E_WORKSPACE and b"scratch" in lib.pack3d_last_error()
+    bs3 = (ctypes.c_int32 * 3)(1, 1, 3)
+    st = lib.pack3d_measure_blocks(ctypes.c_void_p(256), ctypes.byref(pk), bs3, ctypes.c_void_p(256), 64, None,
+                                   ctypes.byref(out))
+    assert st == p3.E_UNSUPPORTED
+
+
+def test_ragged_build_needs_max_blocks():
+    lib = p3.load_library()
+    pk = p3._packing(1, 100, ragged=True)
+    bs = (ctypes.c_int32 * 3)(2, 2, 2)
+    h = ctypes.c_void_p()
+    st = lib.pack3d_build_index(ctypes.c_void_p(256), ctypes.byref(pk), bs, 1, ctypes.c_void_p(256), 1 << 20,
+                                None, ctypes.byref(h))
+    assert st == p3.E_INVALID and b"max_blocks" in lib.pack3d_last_error()

@@ -63,7 +63,7 @@ def test_geometry_errors():
     c = si.raster_coords((4, 4, 8))
     dup = c.copy()
     dup[40] = dup[12]                  # point 12 twice, interior point 40 missing
-    _expect_coords_error(torch.from_numpy(dup[None]), (2, 2, 2), 1, ["duplicate", "packed index 40"])
+    _expect_coords_error(torch.from_numpy(dup[None]), (2, 2, 2), 1, ["duplicate", "local index 40"])
     out = c.copy()
     out[3] = (9, 0, 0)                 # outside: holes in the bounding box
     _expect_coords_error(torch.from_numpy(out[None]), (2, 2, 2), 1, ["fill"])
