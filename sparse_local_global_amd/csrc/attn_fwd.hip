@@ -21,6 +21,10 @@
 // Local tiles come from the compacted neighbour list (a virtual concatenation of
 // the neighbour blocks); summary tiles walk all block means in id order, masking
 // the local blocks (and the padding rows) with an LDS bitmask.
+// bf16 at Dp 32 and 96 (rows without padding) runs k_attn_fwd32d instead: four waves
+// split into query halves and key halves with v_mfma_f32_32x32x16_bf16, tiles copied
+// straight into LDS by buffer loads (no staging registers), the key halves' softmax
+// states merged at the end; the other bf16 widths run the two-wave k_attn_fwd32.
 // Deterministic: fixed reduction order, no atomics.
 #include <cmath>
 
@@ -398,10 +402,249 @@ __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
+// ---- bf16 with direct LDS copies: four wave64s per 64-query tile ----------------------
+// Waves (qh, kh): queries 32qh .. 32qh+31 against key rows 32kh .. 32kh+31 of every tile.
+// The two key halves of a query keep independent online softmax states over disjoint key
+// sets, merged at the end (max of the references, each side rescaled by exp2 of its
+// distance to it): the same sums in another grouping.  Tiles arrive by buffer loads that
+// write LDS directly (no staging registers, no LDS store instructions), two stages deep.
+template <int DP>
+struct FwdStage32 {
+  RowTile<bf16, DP> k, v;
+};
+
+struct FwdSmem32d {
+  int list[kMaxSlots];
+  uint32_t mask[kMaxBlocks / 32];
+  int nloc;
+};
+
+// Two LDS stages (52 KB) leave room for three workgroups per CU, so three waves per SIMD.
+template <int DP, bool ONE_BLOCK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void k_attn_fwd32d(FwdArgs a) {
+  __shared__ FwdSmem32d sm;
+  __shared__ FwdStage32<DP> s0, s1;
+  static_assert(sizeof(f32x4) * (4 * DP / 32) * 64 * 2 <= sizeof(FwdStage32<DP>), "partial outputs fit a stage");
+  static_assert(sizeof(float2) * 64 * 2 <= sizeof(FwdStage32<DP>), "partial statistics fit a stage");
+  const int ntile = a.nblk * a.tiles_per_block;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
+  const int qb = tile / a.tiles_per_block, qsub = tile - qb * a.tiles_per_block;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int N = a.NC, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int nq = bvol < kTile ? bvol : kTile;
+  const int qrow0 = qb * bvol + qsub * kTile;
+  const int mask_words = a.nblkp / 32;
+  const uint32_t* occ = a.occ + (int64_t)b * a.occ_words;
+  if (a.holes && !any_occupied(occ, qrow0, nq)) return;  // no token among the tile's queries
+
+  // summary bitmask: empty blocks start masked, the local blocks are added below
+  for (int i = tid; i < mask_words; i += kThreads) sm.mask[i] = a.holes ? a.emask[(int64_t)b * mask_words + i] : 0u;
+  if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
+  __syncthreads();
+  // uniform by construction; readfirstlane lets the compiler keep the tile branches and
+  // the buffer resources they select scalar
+  const int nloc = __builtin_amdgcn_readfirstlane(sm.nloc);
+  for (int i = tid; i < nloc; i += kThreads) atomicOr(&sm.mask[sm.list[i] >> 5], 1u << (sm.list[i] & 31));
+
+  const int qloc = 32 * qh + col;
+  ColFrag32<DP> f;
+  f.load((const bf16*)a.qrot + (bh * N + qrow0 + qloc) * DP, qloc < nq, half);
+  // the query rows are in registers before any tile copy starts: otherwise the waits for
+  // them at their first use inside the loop also wait for the copies in flight
+  wait_vm<0>();
+  State32<DP> st;
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) st.o[dt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const float c = a.scale_log2;
+
+  const size_t es = sizeof(bf16);
+  const Src krot((const bf16*)a.krot + bh * N * DP, (size_t)N * DP * es);
+  const Src vrow((const bf16*)a.vr + bh * N * DP, (size_t)N * DP * es);
+  const Src kbar((const bf16*)a.kbar + bh * a.nblkp * DP, (size_t)a.nblkp * DP * es);
+  const Src vbar((const bf16*)a.vbar + bh * a.nblkp * DP, (size_t)a.nblkp * DP * es);
+  const int nkeys = nloc * bvol;
+  const int nlt = (nkeys + kTile - 1) / kTile;
+  const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
+  using Dma = TileDma<DP, kThreads>;
+  const Dma dma;
+  auto stage = [&](auto sg) -> FwdStage32<DP>& {
+    if constexpr (decltype(sg)::value == 0) return s0;
+    else return s1;
+  };
+  // (the host-side instantiation of this generic lambda fails silently when one branch
+  // calls issue_at and another issue, so each instantiation uses only one of them)
+  const bf16* kq = (const bf16*)a.krot + bh * N * DP;
+  const bf16* vq = (const bf16*)a.vr + bh * N * DP;
+  const bf16* kbq = (const bf16*)a.kbar + bh * a.nblkp * DP;
+  const bf16* vbq = (const bf16*)a.vbar + bh * a.nblkp * DP;
+  auto issue = [&](auto sg, int t) {
+    FwdStage32<DP>& S = stage(sg);
+    if constexpr (ONE_BLOCK) {
+      // one contiguous run per tensor: select the (uniform) base pointers and build the
+      // buffer resources here, so they stay scalar
+      const bool loc = t < nlt;
+      uint32_t row0 = (uint32_t)(t - nlt) * kTile;
+      if (loc) {
+        const VirtualRows vr(sm.list, bvol, t * kTile);
+        row0 = (uint32_t)(vr.blk0 * bvol + vr.off0);
+      }
+      const size_t bytes = (loc ? (size_t)N : (size_t)a.nblkp) * DP * es;
+      const Src ks(loc ? kq : kbq, bytes), vs(loc ? vq : vbq, bytes);
+      dma.issue_at(ks, S.k, row0 * DP);
+      dma.issue_at(vs, S.v, row0 * DP);
+      return;
+    }
+    if (t < nlt) {
+      const int j0 = t * kTile;
+      const VirtualRows vr(sm.list, bvol, j0);
+      if constexpr (!ONE_BLOCK) {
+        const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
+        dma.issue(krot, S.k, valid, [&](int r) { return vr.row(r) * DP; });
+        dma.issue(vrow, S.v, valid, [&](int r) { return vr.row(r) * DP; });
+      }
+    } else {
+      const int r0 = (t - nlt) * kTile;
+      dma.issue(kbar, S.k, kTile, [&](int r) { return (r0 + r) * DP; });
+      dma.issue(vbar, S.v, kTile, [&](int r) { return (r0 + r) * DP; });
+    }
+  };
+  auto compute = [&](auto sg, int t, const RowsFrag32<DP>& vfr) {
+    const FwdStage32<DP>& S = stage(sg);
+    uint64_t live;
+    if (t < nlt) {
+      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
+      live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+      if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+    } else {
+      const int ts = t - nlt, r0 = ts * kTile;
+      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
+      const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
+      live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
+    }
+    const uint32_t mine = (uint32_t)(live >> (32 * kh));  // this wave's 32 key rows
+    if (mine == 0u) return;  // nothing live here, and m may still be -inf
+    f32x16 sc;
+    score32_rows(S.k, f, sc, col, half, kh);
+    if (mine != ~0u) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * half + (i & 3);
+        if (!((mine >> r) & 1u)) sc[i] = -INFINITY;
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx *= c;
+    if (mx > st.m + kRescale) {
+      const float alpha = fast_exp2(st.m - mx);
+      st.m = mx;
+      st.l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) st.o[dt] *= alpha;
+    }
+    const float mneg = -st.m;
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sc[i], c, mneg));
+      sc[i] = p;
+      ls += p;
+    }
+    st.l += ls;
+    accum32_frag(vfr, sc, st.o);
+  };
+  // Two stages.  The compiler makes every LDS transpose load wait for all copies in
+  // flight, so each step reads its V operands right after the wait for its own tile and
+  // only then starts the copies of the next tile into the stage the barrier freed; those
+  // have the rest of the step to land.
+  auto step = [&](auto sg, int t) {
+    constexpr int SI = decltype(sg)::value;
+    wait_vm<0>();
+    barrier_copies();  // tile t is in stage SI; every wave is done with the other stage
+    RowsFrag32<DP> vfr;
+    read_rows32(stage(sg).v, vfr, lane, half, kh);
+    if (t + 1 < total) issue(Stage_<1 - SI>{}, t + 1);
+    compute(sg, t, vfr);
+  };
+  if (total > 0) issue(Stage_<0>{}, 0);
+  for (int t = 0; t < total; t += 2) {
+    step(Stage_<0>{}, t);
+    if (t + 1 < total) step(Stage_<1>{}, t + 1);
+  }
+  __syncthreads();  // the stages are reused for the merge below
+
+  // merge the key halves: waves kh = 1 leave (m, l, o) in stage 0 ([slot][lane] float4s)
+  // and stage 1 (m, l per lane); waves kh = 0 combine and write the output
+  f32x4* po = (f32x4*)&s0 + qh * (4 * DP / 32) * 64;
+  float2* pml = (float2*)&s1 + qh * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        po[(4 * dt + q) * 64 + lane] = f32x4{st.o[dt][4 * q], st.o[dt][4 * q + 1], st.o[dt][4 * q + 2], st.o[dt][4 * q + 3]};
+    pml[lane] = make_float2(st.m, st.l);
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float2 ml = pml[lane];
+  const float m = fmaxf(st.m, ml.x);
+  // a side that saw no live key has m = -inf, l = 0, o = 0 and weight exp2(-inf) = 0
+  const float w0 = st.m == -INFINITY ? 0.f : fast_exp2(st.m - m);
+  const float w1 = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - m);
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 o1 = po[(4 * dt + q) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.o[dt][4 * q + e] = st.o[dt][4 * q + e] * w0 + o1[e] * w1;
+    }
+  float l = st.l * w0 + ml.y * w1;
+  l += __shfl_xor(l, 32);
+  const int src = qloc < nq ? a.perm[(int64_t)b * N + qrow0 + qloc] : -1;  // -1: empty slot
+  if (src >= 0) {
+    const float inv = 1.0f / l;
+    bf16* orow = (bf16*)a.out + (((int64_t)a.voff[b] + src) * a.H + h) * a.D;
+    if (a.D == DP) {
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(bf16x4*)(orow + 32 * dt + 8 * j + 4 * half) =
+              bf16x4{(bf16)(st.o[dt][4 * j] * inv), (bf16)(st.o[dt][4 * j + 1] * inv),
+                     (bf16)(st.o[dt][4 * j + 2] * inv), (bf16)(st.o[dt][4 * j + 3] * inv)};
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int d = 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (d < a.D) orow[d] = (bf16)(st.o[dt][i] * inv);
+        }
+      }
+    }
+    if (half == 0) a.lse[bh * a.Nmax + src] = m * kLn2 + logf(l);
+  }
+}
+
 template <typename T, int DP>
 void launch_dp(const Dims& d, const FwdArgs& a, dim3 grid, hipStream_t s) {
-  // 32-column waves for bf16 up to Dp = 96 (at Dp = 128 their registers would spill)
-  if constexpr (sizeof(T) == 2 && DP <= 96) {
+  // bf16 rows without padding in LDS (Dp 32, 96): four waves, direct LDS copies
+  if constexpr (sizeof(T) == 2 && (DP == 32 || DP == 96)) {
+    if (d.bvol % kTile == 0) hipLaunchKernelGGL((k_attn_fwd32d<DP, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_fwd32d<DP, false>), grid, dim3(kThreads), 0, s, a);
+  } else if constexpr (sizeof(T) == 2 && DP <= 96) {
+    // 32-column waves for the other bf16 widths up to Dp = 96 (at Dp = 128 their registers would spill)
     if (d.bvol % kTile == 0) hipLaunchKernelGGL((k_attn_fwd32<DP, true>), grid, dim3(kThreads32), 0, s, a);
     else hipLaunchKernelGGL((k_attn_fwd32<DP, false>), grid, dim3(kThreads32), 0, s, a);
   } else {

@@ -295,6 +295,22 @@ __device__ inline void score32_pair(const RowTile<bf16, DP>& t1, const ColFrag32
   }
 }
 
+// Rows 32mt .. 32mt+31 of one score tile: slot i = row 32mt + 8(i/4) + 4h + i%4 against
+// column (lane & 31).
+template <int DP>
+__device__ inline void score32_rows(const RowTile<bf16, DP>& t, const ColFrag32<DP>& f, f32x16& s, int col, int half,
+                                    int mt) {
+  using G = TileGeom<bf16, DP>;
+  const int be = G::base(col & 15, half) + G::off(col & 16, 0);
+  const int bo = G::base(col & 15, 2 + half) + G::off(col & 16, 0);
+  s = f32x16{};
+#pragma unroll
+  for (int k = 0; k < DP / 16; ++k) {
+    const bf16x8 a = *(const bf16x8*)(t.x + (k & 1 ? bo : be) + G::off(32 * mt, 4 * (k >> 1)));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.b[k], s, 0, 0, 0);
+  }
+}
+
 // acc[dt][i] += sum over rows r of block mt of X[r][32dt + 8(i/4) + 4h + i%4] * p[r][lane & 31],
 // p in the slot layout of score32_pair.
 template <int DP>
@@ -318,6 +334,43 @@ __device__ inline void accum32_rows(const RowTile<bf16, DP>& t, const f32x16& p,
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
     }
+  }
+}
+
+// The A operands of accum32_rows (rows 32mt .. 32mt+31 of tile t, read with the LDS
+// transpose load) held in registers, so the reads can happen at a chosen point.
+template <int DP>
+struct RowsFrag32 {
+  bf16x8 a[2][DP / 32];
+};
+
+template <int DP>
+__device__ inline void read_rows32(const RowTile<bf16, DP>& t, RowsFrag32<DP>& v, int lane, int half, int mt) {
+  using G = TileGeom<bf16, DP>;
+  const int lane16 = lane & 15, hi16 = (lane >> 4) & 1;
+  const ColumnBases c0 = column_bases<DP>(4 * half, lane16), c8 = column_bases<DP>(8 + 4 * half, lane16);
+  const int p0 = hi16 ? c0.odd : c0.even;
+  const int p8 = hi16 ? c8.odd : c8.even;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) {
+      const bf16x4 lo = read_tr(t, p0 + G::off(32 * mt + 16 * s, 4 * dt));
+      const bf16x4 hi = read_tr(t, p8 + G::off(32 * mt + 16 * s, 4 * dt));
+      v.a[s][dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+}
+
+// accum32_rows with the operands read beforehand by read_rows32.
+template <int DP>
+__device__ inline void accum32_frag(const RowsFrag32<DP>& v, const f32x16& p, f32x16 (&acc)[DP / 32]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (bf16)p[8 * s + e];
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.a[s][dt], b, acc[dt], 0, 0, 0);
   }
 }
 
