@@ -35,3 +35,19 @@ def dense_masked(q, k, v, c, block, r, rot, with_summaries=True):
     p = torch.softmax(torch.cat([s, t], -1), -1)
     vals = torch.cat([v.transpose(0, 1), vbar.transpose(0, 1)], 1)
     return (p @ vals).transpose(0, 1)
+
+
+def torch_axial_rope(x, c, base=10000.0):
+    """Axial RoPE through torch complex arithmetic: per axis group of width d/3, the pair
+    (k, k + d/6) is one complex number turned by exp(i c_axis base^(-2k/(d/3)))."""
+    n, h, d = x.shape
+    da, half = d // 3, d // 6
+    freq = torch.exp(math.log(base) * (-torch.arange(half, dtype=torch.float64) * 2.0 / da))
+    parts = []
+    for a in range(3):
+        g = x[..., a * da:(a + 1) * da]
+        z = torch.complex(g[..., :half], g[..., half:])
+        w = torch.polar(torch.ones(n, half, dtype=torch.float64), c[:, a, None].double() * freq)
+        zr = z * w[:, None, :]
+        parts += [zr.real, zr.imag]
+    return torch.cat(parts, -1)

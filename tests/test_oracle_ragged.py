@@ -22,7 +22,7 @@ import torch
 
 import oracle
 import synthetic_inputs as si
-from tests.dense_ref import dense_masked
+from tests.dense_ref import dense_masked, torch_axial_rope
 
 CASES = [
     # grids (one per volume), block, radius, occupancy
@@ -184,7 +184,7 @@ def test_backward_against_autograd(mode):
         y = _volume(x, v)
         c = y["coords"][0].long()
         if mode == "axial":
-            rot = lambda t, c=c: _torch_axial_rope(t, c)       # noqa: E731
+            rot = lambda t, c=c: torch_axial_rope(t, c)       # noqa: E731
         else:
             rot = lambda t: t                                    # noqa: E731
         q, k, vv = (y[n][0].double().clone().requires_grad_() for n in ("q", "k", "v"))
@@ -192,22 +192,6 @@ def test_backward_against_autograd(mode):
         (o * y["do"][0].double()).sum().backward()
         for g, ref in zip(grads, (q.grad, k.grad, vv.grad)):
             np.testing.assert_allclose(g[off[v]:off[v + 1]], ref.numpy(), atol=1e-11)
-
-
-def _torch_axial_rope(x, c, base=10000.0):
-    """Axial RoPE through torch complex arithmetic: per axis group of width d/3, the pair
-    (k, k + d/6) is one complex number turned by exp(i c_axis base^(-2k/(d/3)))."""
-    n, h, d = x.shape
-    da, half = d // 3, d // 6
-    freq = torch.exp(math.log(base) * (-torch.arange(half, dtype=torch.float64) * 2.0 / da))
-    parts = []
-    for a in range(3):
-        g = x[..., a * da:(a + 1) * da]
-        z = torch.complex(g[..., :half], g[..., half:])
-        w = torch.polar(torch.ones(n, half, dtype=torch.float64), c[:, a, None].double() * freq)
-        zr = z * w[:, None, :]
-        parts += [zr.real, zr.imag]
-    return torch.cat(parts, -1)
 
 
 def test_geometry_errors():
