@@ -236,6 +236,23 @@ pack3d_status pack3d_backward(const pack3d_index* index, const pack3d_attn* attn
                               void* dk_dev, void* dv_dev, void* workspace_dev,
                               size_t workspace_bytes, int32_t reuse_forward, void* stream);
 
+/* Fused-projection layout ("Geometry Matters in Packed 3D Attention", abstract: the operator
+ * is trained at scale inside a transformer, whose QKV projection emits one [T, 3 * H * D]
+ * matrix).  Same operator as pack3d_forward / pack3d_backward, but q, k and v are read from
+ * one contiguous qkv buffer [T, 3, H, D] (attn->dtype; q = qkv[:, 0], k = qkv[:, 1],
+ * v = qkv[:, 2]) and the backward writes the gradients into one dqkv buffer of that layout,
+ * so no split or concatenation copy is needed around the projection.  out, lse, dout and the
+ * workspace are as in pack3d_forward / pack3d_backward; results are bitwise equal to them.
+ * heads * head_dim * element size must be a multiple of 16 bytes (PACK3D_E_UNSUPPORTED
+ * otherwise); qkv and dqkv must be 16-byte aligned. */
+pack3d_status pack3d_forward_qkv(const pack3d_index* index, const pack3d_attn* attn, const void* qkv_dev,
+                                 const int32_t* coords_dev, void* out_dev, float* lse_dev,
+                                 void* workspace_dev, size_t workspace_bytes, void* stream);
+pack3d_status pack3d_backward_qkv(const pack3d_index* index, const pack3d_attn* attn, const void* qkv_dev,
+                                  const int32_t* coords_dev, const void* out_dev, const float* lse_dev,
+                                  const void* dout_dev, void* dqkv_dev, void* workspace_dev,
+                                  size_t workspace_bytes, int32_t reuse_forward, void* stream);
+
 /* Where the forward leaves its intermediates inside the workspace (byte offsets),
  * for inspection by tests.  All arrays are in canonical order (block-major, raster
  * inside each block; empty slots hold zero rows), elements of attn->dtype except

@@ -60,7 +60,7 @@ using namespace pack3d;
 
 extern "C" const char* pack3d_last_error(void) { return g_msg; }
 
-extern "C" int32_t pack3d_version(void) { return 103; }
+extern "C" int32_t pack3d_version(void) { return 104; }
 
 extern "C" size_t pack3d_workspace_bytes(const pack3d_index* ix, const pack3d_attn* at, int for_backward) {
   if (check_attn(ix, at, "workspace_bytes") != PACK3D_OK) return 0;
@@ -80,42 +80,48 @@ extern "C" pack3d_status pack3d_workspace_views(const pack3d_index* ix, const pa
   return PACK3D_OK;
 }
 
-extern "C" pack3d_status pack3d_forward(const pack3d_index* ix, const pack3d_attn* at, const void* q,
-                                        const void* k, const void* v, const int32_t* coords, void* out,
-                                        float* lse, void* ws, size_t ws_bytes, void* stream) {
-  pack3d_status st = check_attn(ix, at, "forward");
+namespace {
+
+// q, k, v (and dq, dk, dv) are tokens of `in_stride` (`grad_stride`) elements apart.
+pack3d_status run_forward(const pack3d_index* ix, const pack3d_attn* at, const void* q, const void* k,
+                          const void* v, const int32_t* coords, void* out, float* lse, void* ws, size_t ws_bytes,
+                          int64_t in_stride, void* stream, const char* who) {
+  pack3d_status st = check_attn(ix, at, who);
   if (st != PACK3D_OK) return st;
   if (!q || !k || !v || !coords || !out || !lse || !ws)
-    return set_error(PACK3D_E_INVALID, "forward: null pointer argument");
+    return set_error(PACK3D_E_INVALID, "%s: null pointer argument", who);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws))
-    return set_error(PACK3D_E_INVALID, "forward: q, k, v, out and workspace must be 16-byte aligned");
+    return set_error(PACK3D_E_INVALID, "%s: q, k, v, out and workspace must be 16-byte aligned", who);
   Dims d = make_dims(ix, at);
+  d.in_stride = in_stride;
   Workspace w = workspace_layout(d);
   if (ws_bytes < w.fwd_total)
-    return set_error(PACK3D_E_WORKSPACE, "forward: workspace %zu bytes < %zu needed", ws_bytes, w.fwd_total);
+    return set_error(PACK3D_E_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, w.fwd_total);
   hipStream_t s = (hipStream_t)stream;
   st = launch_rope_pool(d, ix, at, q, k, v, coords, (char*)ws, w, "rope_pool", s);
   if (st != PACK3D_OK) return st;
   return launch_attn_fwd(d, ix, at, (const char*)ws, w, out, lse, s);
 }
 
-extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_attn* at, const void* q,
-                                         const void* k, const void* v, const int32_t* coords,
-                                         const void* out, const float* lse, const void* dout, void* dq,
-                                         void* dk, void* dv, void* ws, size_t ws_bytes, int32_t reuse_forward,
-                                         void* stream) {
-  pack3d_status st = check_attn(ix, at, "backward");
+pack3d_status run_backward(const pack3d_index* ix, const pack3d_attn* at, const void* q, const void* k,
+                           const void* v, const int32_t* coords, const void* out, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                           int32_t reuse_forward, int64_t in_stride, int64_t grad_stride, void* stream,
+                           const char* who) {
+  pack3d_status st = check_attn(ix, at, who);
   if (st != PACK3D_OK) return st;
   if (!q || !k || !v || !coords || !out || !lse || !dout || !dq || !dk || !dv || !ws)
-    return set_error(PACK3D_E_INVALID, "backward: null pointer argument");
+    return set_error(PACK3D_E_INVALID, "%s: null pointer argument", who);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(ws))
-    return set_error(PACK3D_E_INVALID, "backward: q, k, v, out, dout and workspace must be 16-byte aligned");
+    return set_error(PACK3D_E_INVALID, "%s: q, k, v, out, dout and workspace must be 16-byte aligned", who);
   Dims d = make_dims(ix, at);
+  d.in_stride = in_stride;
+  d.grad_stride = grad_stride;
   Workspace w = workspace_layout(d);
   if (ws_bytes < w.bwd_total)
-    return set_error(PACK3D_E_WORKSPACE, "backward: workspace %zu bytes < %zu needed", ws_bytes, w.bwd_total);
+    return set_error(PACK3D_E_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, w.bwd_total);
   if (reuse_forward != 0 && reuse_forward != 1)
-    return set_error(PACK3D_E_INVALID, "backward: reuse_forward must be 0 or 1");
+    return set_error(PACK3D_E_INVALID, "%s: reuse_forward must be 0 or 1", who);
   hipStream_t s = (hipStream_t)stream;
   if (!reuse_forward) {
     // recompute the rotated and pooled operands into the forward part of the workspace
@@ -123,4 +129,63 @@ extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_at
     if (st != PACK3D_OK) return st;
   }
   return launch_attn_bwd(d, ix, at, coords, out, lse, dout, dq, dk, dv, (char*)ws, w, s);
+}
+
+// The fused [T, 3, H, D] layout needs every head block (H * D elements) to start on a
+// 16-byte boundary.
+pack3d_status check_fused(const pack3d_attn* at, const char* who) {
+  if (!at) return set_error(PACK3D_E_INVALID, "%s: null attention parameters", who);
+  const size_t es = at->dtype == PACK3D_BF16 ? 2 : 4;
+  if (((size_t)at->heads * at->head_dim * es) % 16)
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: heads * head_dim * element size must be a multiple of 16 bytes",
+                     who);
+  return PACK3D_OK;
+}
+
+}  // namespace
+
+extern "C" pack3d_status pack3d_forward(const pack3d_index* ix, const pack3d_attn* at, const void* q,
+                                        const void* k, const void* v, const int32_t* coords, void* out,
+                                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const int64_t hd = at ? (int64_t)at->heads * at->head_dim : 0;
+  return run_forward(ix, at, q, k, v, coords, out, lse, ws, ws_bytes, hd, stream, "forward");
+}
+
+extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_attn* at, const void* q,
+                                         const void* k, const void* v, const int32_t* coords,
+                                         const void* out, const float* lse, const void* dout, void* dq,
+                                         void* dk, void* dv, void* ws, size_t ws_bytes, int32_t reuse_forward,
+                                         void* stream) {
+  const int64_t hd = at ? (int64_t)at->heads * at->head_dim : 0;
+  return run_backward(ix, at, q, k, v, coords, out, lse, dout, dq, dk, dv, ws, ws_bytes, reuse_forward, hd, hd,
+                      stream, "backward");
+}
+
+extern "C" pack3d_status pack3d_forward_qkv(const pack3d_index* ix, const pack3d_attn* at, const void* qkv,
+                                            const int32_t* coords, void* out, float* lse, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  pack3d_status st = check_fused(at, "forward_qkv");
+  if (st != PACK3D_OK) return st;
+  if (!qkv) return set_error(PACK3D_E_INVALID, "forward_qkv: null pointer argument");
+  const int64_t hd = (int64_t)at->heads * at->head_dim;
+  const size_t part = (size_t)hd * (at->dtype == PACK3D_BF16 ? 2 : 4);
+  const char* base = (const char*)qkv;
+  return run_forward(ix, at, base, base + part, base + 2 * part, coords, out, lse, ws, ws_bytes, 3 * hd, stream,
+                     "forward_qkv");
+}
+
+extern "C" pack3d_status pack3d_backward_qkv(const pack3d_index* ix, const pack3d_attn* at, const void* qkv,
+                                             const int32_t* coords, const void* out, const float* lse,
+                                             const void* dout, void* dqkv, void* ws, size_t ws_bytes,
+                                             int32_t reuse_forward, void* stream) {
+  pack3d_status st = check_fused(at, "backward_qkv");
+  if (st != PACK3D_OK) return st;
+  if (!qkv || !dqkv) return set_error(PACK3D_E_INVALID, "backward_qkv: null pointer argument");
+  if (!aligned16(dqkv)) return set_error(PACK3D_E_INVALID, "backward_qkv: dqkv must be 16-byte aligned");
+  const int64_t hd = (int64_t)at->heads * at->head_dim;
+  const size_t part = (size_t)hd * (at->dtype == PACK3D_BF16 ? 2 : 4);
+  const char* base = (const char*)qkv;
+  char* g = (char*)dqkv;
+  return run_backward(ix, at, base, base + part, base + 2 * part, coords, out, lse, dout, g, g + part, g + 2 * part,
+                      ws, ws_bytes, reuse_forward, 3 * hd, 3 * hd, stream, "backward_qkv");
 }

@@ -50,6 +50,7 @@ struct BwdArgs {
   // NC canonical rows per volume, Nmax the lse stride, holes: empty slots exist
   int B, NC, Nmax, H, D, Dp, nblk, nblkp, bvol, slots, radius, tiles_per_block, with_summaries, chunks;
   int holes, occ_words;
+  int64_t grad_stride;  // elements between consecutive tokens of dq, dk, dv
   int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
   int bz, by, bx;
   float scale, scale_log2;
@@ -156,7 +157,7 @@ __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, in
       if (k < half) v = v * cs.x + st[r * sts + col + half] * cs.y;      // y1 c + y2 s
       else v = -st[r * sts + col - half] * cs.y + v * cs.x;              // -y1 s + y2 c
     }
-    dst[((tok0 + s_src[r]) * a.H + h) * D + col] = (T)v;
+    dst[(tok0 + s_src[r]) * a.grad_stride + (int64_t)h * D + col] = (T)v;
   }
   __syncthreads();  // s_src / s_rel are rewritten by the next call
 }
@@ -522,7 +523,7 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
         acc[(m + 6) / 4][4 * ((m + 6) % 4) + e] = -y1 * t.y + y2 * t.x;
       }
   }
-  bf16* dst = (bf16*)(qh == 0 ? a.dk : a.dv) + ((tok0 + src) * a.H + h) * 96;
+  bf16* dst = (bf16*)(qh == 0 ? a.dk : a.dv) + (tok0 + src) * a.grad_stride + (int64_t)h * 96;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -745,7 +746,7 @@ __device__ inline void dq_epilogue96(const BwdArgs& a, f32x4 (&dq)[6], int b, in
   const int64_t tok0 = a.voff[b];
   const int32_t* g = a.geom + b * G_FIELDS;
   const int32_t* c = a.coords + (tok0 + src) * 3;
-  T* dst = (T*)a.dq + ((tok0 + src) * a.H + h) * 96;
+  T* dst = (T*)a.dq + (tok0 + src) * a.grad_stride + (int64_t)h * 96;
   if (a.pos_mode == PACK3D_POS_PACKED_1D) {  // pairs (k, k + 48): dq[dt] with dq[dt + 3]
     const float2* cs = a.tab + (int64_t)src * 48 + 4 * grp;
 #pragma unroll
@@ -973,6 +974,7 @@ pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3
   a.coords = coords; a.perm = ix->perm; a.nbr = ix->nbr; a.geom = ix->geom;
   a.voff = ix->voff; a.count = ix->count; a.occ = ix->occ; a.emask = ix->emask;
   a.holes = d.holes; a.occ_words = ix->occ_words;
+  a.grad_stride = d.grad_stride;
   a.B = d.B; a.NC = d.NC; a.Nmax = d.Nmax; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.slots = d.slots; a.radius = ix->radius;
   a.tiles_per_block = d.bvol > kTile ? d.bvol / kTile : 1;

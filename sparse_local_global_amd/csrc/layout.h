@@ -20,6 +20,9 @@ struct Dims {
   // (k, k + half) each, table of `trows` angle rows (positions) x half
   int pos_mode, groups, gw, half, trows;
   size_t esize;  // bytes per element of the activation dtype
+  // elements between consecutive tokens of the q, k, v inputs and of the dq, dk, dv
+  // outputs: H * D for separate [T, H, D] tensors, 3 * H * D inside one [T, 3, H, D] buffer
+  int64_t in_stride, grad_stride;
 };
 
 inline Dims make_dims(const pack3d_index* ix, const pack3d_attn* at) {
@@ -38,6 +41,7 @@ inline Dims make_dims(const pack3d_index* ix, const pack3d_attn* at) {
   d.half = d.gw / 2;
   d.trows = d.pos_mode == PACK3D_POS_AXIAL ? d.emax : (d.pos_mode == PACK3D_POS_PACKED_1D ? d.Nmax : 1);
   d.esize = at->dtype == PACK3D_BF16 ? 2 : 4;
+  d.in_stride = d.grad_stride = (int64_t)d.H * d.D;
   return d;
 }
 

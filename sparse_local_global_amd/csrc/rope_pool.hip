@@ -52,6 +52,7 @@ struct RopeArgs {
   const float2* tab;
   void* qrot; void* krot; void* vr; void* kbar; void* vbar;
   int NC, H, D, Dp, nblk, nblkp, bvol, heads_per_group, holes;
+  int64_t in_stride;  // elements between consecutive tokens of q, k, v
   int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
 };
 
@@ -115,11 +116,11 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         const int col1 = ax * gw + p * VEC, col2 = col1 + half;
         Vec<T, VEC> q1, q2, k1, k2;
         if (src >= 0) {
-          const int64_t in_row = (tok0 + src) * H + h;
-          q1 = *(const Vec<T, VEC>*)(q + in_row * D + col1);
-          q2 = *(const Vec<T, VEC>*)(q + in_row * D + col2);
-          k1 = *(const Vec<T, VEC>*)(k + in_row * D + col1);
-          k2 = *(const Vec<T, VEC>*)(k + in_row * D + col2);
+          const int64_t in_row = (tok0 + src) * a.in_stride + (int64_t)h * D;
+          q1 = *(const Vec<T, VEC>*)(q + in_row + col1);
+          q2 = *(const Vec<T, VEC>*)(q + in_row + col2);
+          k1 = *(const Vec<T, VEC>*)(k + in_row + col1);
+          k2 = *(const Vec<T, VEC>*)(k + in_row + col2);
         } else {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) q1.v[e] = q2.v[e] = k1.v[e] = k2.v[e] = from_f<T>(0.f);
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         const int src = s_src[t0 + tok];
         Vec<T, VEC> x;
         if (src >= 0) {
-          x = *(const Vec<T, VEC>*)(v + ((tok0 + src) * H + h) * D + col);
+          x = *(const Vec<T, VEC>*)(v + (tok0 + src) * a.in_stride + (int64_t)h * D + col);
         } else {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) x.v[e] = from_f<T>(0.f);
@@ -246,6 +247,7 @@ pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack
   a.voff = ix->voff; a.count = ix->count; a.holes = d.holes;
   a.tab = (const float2*)(ws + w.rope);
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
+  a.in_stride = d.in_stride;
   a.NC = d.NC; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.pos_mode = d.pos_mode; a.groups = d.groups; a.gw = d.gw; a.half = d.half; a.trows = d.trows;
   // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all

@@ -75,6 +75,10 @@ EXPORTS = {
                        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pack3d_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 10
                         + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]),
+    "pack3d_forward_qkv": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 4
+                           + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pack3d_backward_qkv": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 6
+                            + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]),
     "pack3d_workspace_views": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn), ctypes.POINTER(Views)]),
     "pack3d_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
     "pack3d_profile_read": (ctypes.c_int32, [ctypes.c_char_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
@@ -325,6 +329,56 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
     return dq, dk, dv
 
 
+def forward_qkv(index: Index, qkv, coords, *, rope_base=10000.0, scale=None, with_summaries=True,
+                workspace: torch.Tensor | None = None, out=None, lse=None, position_mode="axial"):
+    """PACK3D forward from one fused projection output qkv [T, 3, H, D] (q, k, v = qkv[:, 0],
+    qkv[:, 1], qkv[:, 2]; T = every token of the batch).  Returns (out [T, H, D], lse fp32
+    [B, H, Nmax])."""
+    lib = load_library()
+    t, three, h, d = qkv.shape
+    if three != 3 or t != index.total:
+        raise Pack3DError(E_INVALID, f"qkv must be [{index.total}, 3, H, D]")
+    attn = make_attn(qkv.dtype, h, d, rope_base, scale, with_summaries, position_mode)
+    _check_act("qkv", qkv, (t, 3, h, d), qkv.dtype)
+    need = workspace_bytes(index, attn)
+    if need == 0:
+        raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
+    if out is None:
+        out = torch.empty((t, h, d), dtype=qkv.dtype, device=qkv.device)
+    if lse is None:
+        lse = torch.empty((index.batch, h, index.tokens), dtype=torch.float32, device=qkv.device)
+    _check(lib.pack3d_forward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()),
+                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                  ctypes.c_void_p(_stream())))
+    return out, lse
+
+
+def backward_qkv(index: Index, qkv, coords, out, lse, dout, *, rope_base=10000.0, scale=None,
+                 with_summaries=True, workspace: torch.Tensor | None = None, reuse_forward: bool = False,
+                 position_mode="axial"):
+    """Gradient dqkv [T, 3, H, D] of sum(out * dout) with respect to the fused qkv input."""
+    lib = load_library()
+    t, _, h, d = qkv.shape
+    attn = make_attn(qkv.dtype, h, d, rope_base, scale, with_summaries, position_mode)
+    _check_act("qkv", qkv, (index.total, 3, h, d), qkv.dtype)
+    for name, x in (("out", out), ("dout", dout)):
+        _check_act(name, x, (index.total, h, d), qkv.dtype)
+    need = workspace_bytes(index, attn, True)
+    if need == 0:
+        raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
+    if workspace is None:
+        if reuse_forward:
+            raise Pack3DError(E_INVALID, "reuse_forward needs the forward's workspace")
+        workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
+    dqkv = torch.empty_like(qkv)
+    _check(lib.pack3d_backward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()), _ptr(out),
+                                   _ptr(lse.contiguous()), _ptr(dout), _ptr(dqkv), _ptr(workspace),
+                                   workspace.numel(), 1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
+    return dqkv
+
+
 def workspace_views(index: Index, q_shape, dtype, workspace: torch.Tensor, rope_base=10000.0,
                     position_mode="axial") -> dict:
     """Tensor views of the forward intermediates left in ``workspace`` (canonical rows:
@@ -410,3 +464,39 @@ def attention(q, k, v, index: Index, coords, rope_base=10000.0, scale=None, with
               position_mode="axial"):
     """PACK3D attention with autograd support (position_mode: see make_attn)."""
     return Pack3DAttention.apply(q, k, v, index, coords, rope_base, scale, with_summaries, position_mode)
+
+
+class Pack3DAttentionQKV(torch.autograd.Function):
+    """Autograd wrapper over the fused-projection entry points: qkv [T, 3, H, D] -> out [T, H, D]."""
+
+    @staticmethod
+    def forward(ctx, qkv, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True,
+                position_mode="axial"):
+        qkv = qkv.contiguous()
+        attn = make_attn(qkv.dtype, qkv.shape[2], qkv.shape[3], rope_base, scale, with_summaries, position_mode)
+        need = workspace_bytes(index, attn, True)
+        if need == 0:
+            raise Pack3DError(E_UNSUPPORTED, load_library().pack3d_last_error().decode())
+        ws = torch.empty(need, dtype=torch.uint8, device=qkv.device)
+        out, lse = forward_qkv(index, qkv, coords, rope_base=rope_base, scale=scale, with_summaries=with_summaries,
+                               workspace=ws, position_mode=position_mode)
+        ctx.save_for_backward(qkv, out, lse)
+        ctx.index, ctx.coords, ctx.workspace = index, coords, ws
+        ctx.opts = (rope_base, scale, with_summaries, position_mode)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        qkv, out, lse = ctx.saved_tensors
+        rope_base, scale, with_summaries, position_mode = ctx.opts
+        dqkv = backward_qkv(ctx.index, qkv, ctx.coords, out, lse, dout.contiguous(), rope_base=rope_base, scale=scale,
+                            with_summaries=with_summaries, workspace=ctx.workspace, reuse_forward=True,
+                            position_mode=position_mode)
+        ctx.workspace = None
+        return dqkv, None, None, None, None, None, None
+
+
+def attention_qkv(qkv, index: Index, coords, rope_base=10000.0, scale=None, with_summaries=True,
+                  position_mode="axial"):
+    """PACK3D attention on a fused projection output qkv [T, 3, H, D], with autograd."""
+    return Pack3DAttentionQKV.apply(qkv, index, coords, rope_base, scale, with_summaries, position_mode)

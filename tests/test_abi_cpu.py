@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     lib = p3.load_library()
     names = _declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) <= set(p3.EXPORTS)
@@ -40,7 +40,7 @@ def test_exported_symbols_in_dynamic_table():
 
 def test_version_and_last_error():
     lib = p3.load_library()
-    assert lib.pack3d_version() == 103
+    assert lib.pack3d_version() == 104
     assert isinstance(lib.pack3d_last_error(), bytes)
 
 
