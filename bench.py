@@ -137,6 +137,43 @@ def ragged_step(name: str, steps: int, warmup: int) -> dict:
             "kernels_avg_ms": {k: tt / max(n, 1) for k, (n, tt) in prof.items()}}
 
 
+def block_step(w, coords, steps: int, warmup: int) -> dict:
+    """Training step of one pre-norm transformer block around the operator at the workload's
+    shapes (C = H * D, MLP 4 C, bf16, random init): forward, then backward for the input and
+    every weight.  The projections are hipBLASLt GEMMs through torch; the operator runs from
+    the QKV projection's output in place."""
+    import torch
+    import sparse_local_global_amd.pack3d as p3
+    from sparse_local_global_amd.block import Pack3DBlock
+    c = w.heads * w.head_dim
+    torch.manual_seed(0)
+    m = Pack3DBlock(c, w.heads, rope_base=w.rope_base, device="cuda:0", dtype=torch.bfloat16)
+    x = torch.randn((w.batch, w.tokens, c), device="cuda:0", dtype=torch.bfloat16).requires_grad_()
+    dy = torch.randn_like(x)
+    ix = p3.build_index(coords, w.block, w.radius, order_hint=w.packing)
+
+    def step():
+        m.zero_grad(set_to_none=True)
+        x.grad = None
+        (m(x, ix, coords) * dy).sum().backward()
+
+    for _ in range(warmup):
+        step()
+    ms = time_region(step, steps)
+    p3.profile_reset()
+    p3.profile_enable(True)
+    time_region(step, steps)
+    prof = p3.profile_read()
+    p3.profile_enable(False)
+    op_ms = sum(t for _, t in prof.values()) / steps
+    tokens = w.batch * w.tokens
+    gemm_flop = 3 * 2.0 * tokens * c * (3 * c + c + 2 * 4 * c)   # forward + two backward products each
+    return {"model": f"pre-norm block, C={c}, heads={w.heads}, MLP 4C, bf16", "tokens": tokens,
+            "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3), "operator_ms_per_step": op_ms,
+            "operator_share": op_ms / ms, "gemm_flop_per_step": gemm_flop,
+            "other_tflops": gemm_flop / ((ms - op_ms) * 1e-3) / 1e12}
+
+
 def cpu_baseline(w, x, sample_blocks: int) -> dict:
     """The fp64 oracle on the host cores: all heads of the first `sample_blocks` query blocks of each volume."""
     import oracle  # test infrastructure, used only for this reported baseline
@@ -167,6 +204,8 @@ def main(argv=None) -> int:
                     help="rotation of the timed step (axial grid-coordinate RoPE is the method)")
     ap.add_argument("--no-mode-compare", action="store_true",
                     help="skip timing the step under the other position modes")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip timing the transformer-block training step around the operator")
     ap.add_argument("--no-ragged", action="store_true",
                     help="skip timing the step on the ragged varlen stand-in (partial blocks, holes)")
     ap.add_argument("--cpu-sample-blocks", type=int, default=256)
@@ -345,6 +384,10 @@ def main(argv=None) -> int:
     }
     if modes:
         result["position_modes"] = modes
+    if not args.no_block and with_bwd:
+        blk = block_step(w, xd["coords"], args.steps, args.warmup)
+        log(f"bench: transformer block step {blk['ms_per_step']:.3f} ms (operator {blk['operator_ms_per_step']:.3f} ms)")
+        result["block"] = blk
     if not args.no_ragged and with_bwd:
         rg = ragged_step("65k-ragged", args.steps, args.warmup)
         log(f"bench: ragged 65k-ragged: step {rg['ms_per_step']:.3f} ms ({rg['tokens']} tokens)")

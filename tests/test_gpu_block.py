@@ -120,3 +120,41 @@ def test_block_autograd_fused_gradient_layout():
     ref = oracle.backward(x["q"], x["k"], x["v"], coords, dout.cpu()[None], w.block, w.radius)
     for s in range(3):
         assert np.abs(qkv.grad[:, s].double().cpu().numpy() - ref[s][0]).max() < 1e-5, s
+
+
+def test_block_65k_forward_sampled():
+    """The block at the 65k shapes (2 x 65,536 tokens, C = 768, bf16): outputs of sampled
+    query blocks against the oracle block (projections of every token in fp64, the operator
+    on the sampled query blocks only)."""
+    w = si.WORKLOADS["65k"]
+    dtype = torch.bfloat16
+    say("block 65k forward")
+    c = w.heads * w.head_dim
+    coords = si.make_inputs(si.small_workload(grid=w.grid, block=w.block, heads=1, head_dim=6, batch=w.batch,
+                                              packing=w.packing, seed=w.seed), torch.float32)["coords"]
+    gen = np.random.default_rng(95)
+    x = torch.from_numpy(gen.standard_normal((w.batch, w.tokens, c), dtype=np.float32)).to(dtype)
+    params = {k: v.to(dtype).double() for k, v in ob.init_params(c, seed=95).items()}
+    m = Pack3DBlock(c, w.heads, device=DEV, dtype=dtype)
+    m.load_oracle_params(params)
+    cd = coords.to(DEV)
+    ix = p3.build_index(cd, w.block, w.radius)
+    with torch.no_grad():
+        y = m(x.to(DEV), ix, cd).double().cpu()
+    torch.cuda.synchronize()
+    nb = tuple(g // b for g, b in zip(w.grid, w.block))
+    from tests.gpu_cases import sample_blocks
+    blocks = sample_blocks(nb, count=6, seed=w.seed)
+    xr = x.double()
+    with torch.no_grad():
+        qkv = ob.layer_norm(xr, params["ln1_w"], params["ln1_b"]) @ params["qkv"].T
+        q, k, v = (qkv[..., s * c:(s + 1) * c].reshape(w.batch, w.tokens, w.heads, w.head_dim) for s in range(3))
+        o, _ = oracle.forward(q.numpy(), k.numpy(), v.numpy(), coords.numpy(), w.block, w.radius,
+                              query_blocks=blocks)
+        rows = ~np.isnan(o[..., 0, 0])                       # [B, N] sampled tokens
+        a = torch.from_numpy(o[rows].reshape(-1, c))
+        x1 = xr[torch.from_numpy(rows)] + a @ params["proj"].T
+        yr = x1 + ob.gelu(ob.layer_norm(x1, params["ln2_w"], params["ln2_b"]) @ params["fc1"].T) @ params["fc2"].T
+    err = _rel_err(y[torch.from_numpy(rows)], yr)
+    say(f"  65k block: {int(rows.sum())} sampled tokens, relative error {err:.2e}")
+    assert err < BLOCK_TOL[dtype]
