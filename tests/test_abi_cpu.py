@@ -145,3 +145,17 @@ def test_ragged_build_needs_max_blocks():
     st = lib.pack3d_build_index(ctypes.c_void_p(256), ctypes.byref(pk), bs, 1, ctypes.c_void_p(256), 1 << 20,
                                 None, ctypes.byref(h))
     assert st == p3.E_INVALID and b"max_blocks" in lib.pack3d_last_error()
+
+
+def test_fused_entry_points_argument_errors():
+    lib = p3.load_library()
+    at = p3.Attn(p3.BF16, 8, 96, 10000.0, 0.0, 1)
+    st = lib.pack3d_forward_qkv(None, ctypes.byref(at), None, None, None, None, None, 0, None)
+    assert st == p3.E_INVALID and b"null" in lib.pack3d_last_error()
+    st = lib.pack3d_backward_qkv(None, ctypes.byref(at), None, None, None, None, None, None, None, 0, 0, None)
+    assert st == p3.E_INVALID
+    odd = p3.Attn(p3.BF16, 1, 6, 10000.0, 0.0, 1)            # one head of 6 bf16: 12 bytes per head block
+    st = lib.pack3d_forward_qkv(None, ctypes.byref(odd), ctypes.c_void_p(256), None, None, None, None, 0, None)
+    assert st == p3.E_UNSUPPORTED and b"16 bytes" in lib.pack3d_last_error()
+    st = lib.pack3d_forward_qkv(None, None, ctypes.c_void_p(256), None, None, None, None, 0, None)
+    assert st == p3.E_INVALID
