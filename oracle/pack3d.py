@@ -513,7 +513,8 @@ def dense_attention(q, k, v, coords, *, rope_base=10000.0, scale=None, position_
 # --------------------------------------------------------------------------
 
 def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.0, scale=None,
-             with_summaries=True, volumes=None, heads=None, position_mode="axial", ragged=False, offsets=None):
+             with_summaries=True, volumes=None, heads=None, position_mode="axial", ragged=False, offsets=None,
+             query_blocks=None):
     """Gradients (dq, dk, dv) fp64 of sum(o * do) w.r.t. unrotated q, k, v, shaped like q
     (layouts as in ``forward``).
 
@@ -526,7 +527,8 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
       dq = R(c)^T dQ~, dk = R(c)^T dK~  (the mean pooling broadcasts 1/n_b to the n_b
       tokens present in block b; n_b = |b| on a full grid).
     ``volumes`` / ``heads`` restrict the work (other entries are NaN); R is the rotation of
-    ``position_mode``.
+    ``position_mode``.  With ``query_blocks`` (block ids, as in ``forward``) only dq of
+    those query blocks is returned: dk and dv need every query, so they are all NaN.
     """
     q, k, v, coords, vols = _prepare(q, k, v, coords, block_shape, local_radius, rope_base,
                                      position_mode=position_mode, ragged=ragged, offsets=offsets)
@@ -549,11 +551,14 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
         dvc = np.zeros_like(vc_all)
         dkbar = np.zeros_like(kbar)
         dvbar = np.zeros_like(vbar)
-        for qb in range(nblk):
+        qbs = range(nblk) if query_blocks is None else [qb for qb in query_blocks if qb < nblk]
+        done = np.zeros(present.shape, dtype=bool)               # canonical rows whose dq was computed
+        for qb in qbs:
             rows = np.arange(qb * bvol, (qb + 1) * bvol)
             rows = rows[present[rows]]
             if rows.size == 0:
                 continue
+            done[rows] = True
             local = _local_blocks(ix, qb)
             krows = _key_rows(local, bvol, present)
             qt = qt_all[rows].transpose(1, 0, 2)                 # [H, bq, D]
@@ -597,8 +602,12 @@ def backward(q, k, v, coords, do, block_shape, local_radius, *, rope_base=10000.
         c = rcs[vi][src]
         dq_c = rotate(dqt[live], c, src, rope_base, position_mode, inverse=True)
         dk_c = rotate(dkt[live], c, src, rope_base, position_mode, inverse=True)
-        for g, val in zip(grads, (dq_c, dk_c, dvc[live])):
+        for gi, (g, val) in enumerate(zip(grads, (dq_c, dk_c, dvc[live]))):
             tmp = np.full((ix["n"], len(hsel), d), np.nan)
-            tmp[src] = val
+            if query_blocks is None:
+                tmp[src] = val
+            elif gi == 0:
+                keep = done[live]
+                tmp[src[keep]] = val[keep]
             g[vi][:, hsel] = tmp
     return tuple(_join(g, offsets) for g in grads)

@@ -122,3 +122,64 @@ def test_backward_repacking_equivariance_bitwise():
         else:
             for a, b in zip(g, ref):
                 assert np.array_equal(a, b), packing
+
+
+def test_backward_query_block_sampling_matches_full():
+    """dq of sampled query blocks equals the full pass bitwise; dk and dv are not returned."""
+    w = si.small_workload(grid=(4, 4, 6), block=(2, 2, 2), head_dim=12, heads=2, seed=35, batch=2)
+    x = si.make_inputs(w, torch.float32, with_grad=True)
+    full = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, 1)
+    part = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, 1, query_blocks=[0, 4, 11])
+    ok = ~np.isnan(part[0])
+    assert ok.sum() == 2 * 3 * 8 * 2 * 12
+    assert np.array_equal(part[0][ok], full[0][ok])
+    assert np.isnan(part[1]).all() and np.isnan(part[2]).all()
+    y = si.make_ragged_inputs([(5, 4, 6), (3, 6, 4)], 2, 12, occupancy=0.7, seed=36, with_grad=True)
+    off = y["offsets"].numpy()
+    full = oracle.backward(y["q"], y["k"], y["v"], y["coords"], y["do"], (2, 2, 2), 1, ragged=True, offsets=off)
+    part = oracle.backward(y["q"], y["k"], y["v"], y["coords"], y["do"], (2, 2, 2), 1, ragged=True, offsets=off,
+                           query_blocks=[1, 7])
+    ok = ~np.isnan(part[0])
+    assert 0 < ok.sum() < ok.size
+    assert np.array_equal(part[0][ok], full[0][ok])
+
+
+def _conservation(q, k, v, c, do, block, r, with_s=True, offsets=None, ragged=False):
+    """(sum_j dv_j - sum_i do_i, sum_j R_j dk_j) per volume, fp64 [H, D] each."""
+    dq, dk, dv = oracle.backward(q, k, v, c, do, block, r, with_summaries=with_s, offsets=offsets, ragged=ragged)
+    res = []
+    if offsets is None:
+        vols = [(dk[b], dv[b], do[b].double(), c[b]) for b in range(q.shape[0])]
+    else:
+        vols = [(dk[a:e], dv[a:e], do[a:e].double(), c[a:e]) for a, e in zip(offsets[:-1], offsets[1:])]
+    for dkv, dvv, dov, cv in vols:
+        rel = torch.as_tensor(cv).long()
+        rel = rel - rel.min(0).values
+        rot = _rope_torch(torch.from_numpy(dkv), rel, 10000.0)
+        res.append((dvv.sum(0) - dov.numpy().sum(0), rot.sum(0).numpy()))
+    return res
+
+
+@pytest.mark.parametrize("grid,block,r,with_s", [((4, 6, 8), (2, 2, 2), 1, True),
+                                                 ((4, 6, 8), (2, 2, 2), 1, False),
+                                                 ((4, 4, 8), (2, 2, 4), 0, True)])
+def test_backward_conservation_laws(grid, block, r, with_s):
+    """Each query's softmax weights sum to one, so (i) the value gradients add up to the sum of
+    dO over queries, and (ii) the rotated key gradients R_j dk_j add up to zero (every score row
+    has zero-sum dS); block means hand each summary's gradient to its members in full."""
+    w = si.small_workload(grid=grid, block=block, head_dim=12, heads=2, seed=37, batch=2)
+    x = si.make_inputs(w, torch.float32, with_grad=True)
+    do = x["do"] + 0.75                 # a mean offset makes the value-gradient sum large
+    for dv_gap, dk_sum in _conservation(x["q"], x["k"], x["v"], x["coords"], do, block, r, with_s):
+        assert np.abs(dv_gap).max() < 1e-11
+        assert np.abs(dk_sum).max() < 1e-11
+
+
+def test_backward_conservation_laws_ragged():
+    y = si.make_ragged_inputs([(5, 4, 6), (3, 6, 4)], 2, 12, occupancy=0.6, seed=38, with_grad=True)
+    off = y["offsets"].numpy()
+    do = y["do"] + 0.75
+    for dv_gap, dk_sum in _conservation(y["q"], y["k"], y["v"], y["coords"], do, (2, 2, 2), 1,
+                                        offsets=off, ragged=True):
+        assert np.abs(dv_gap).max() < 1e-11
+        assert np.abs(dk_sum).max() < 1e-11

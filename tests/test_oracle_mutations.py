@@ -208,3 +208,22 @@ def test_unpool_by_block_volume_fails_ragged_autograd(monkeypatch):
     o = dense_masked(q, k, v, x["coords"].long(), (2, 2, 3), 1, lambda t: t)
     (o * x["do"].double()).sum().backward()
     assert np.abs(dk[0] - k.grad.numpy()).max() > 1e-4
+
+
+def test_unscaled_or_unrotated_gradients_fail_conservation(monkeypatch):
+    from tests.test_oracle_backward import _conservation
+    w = _w(grid=(4, 4, 8), head_dim=12, heads=2)
+    x = si.make_inputs(w, torch.float32, with_grad=True)
+    do = x["do"] + 0.75
+    args = (x["q"], x["k"], x["v"], x["coords"], do, w.block, 1)
+    gap, rot = _conservation(*args)[0]
+    assert np.abs(gap).max() < 1e-11 and np.abs(rot).max() < 1e-11
+    with monkeypatch.context() as m:
+        # plant: every block member receives the whole summary gradient (no 1/n_b)
+        m.setattr(op, "unpool_grad", lambda dbar, bvol, count=None: np.repeat(dbar, bvol, axis=0))
+        gap, rot = _conservation(*args)[0]
+        assert np.abs(gap).max() > 1e-3 and np.abs(rot).max() > 1e-3
+    with monkeypatch.context() as m:
+        m.setattr(op, "rope", _rope_forward_only)       # plant: RoPE transpose skipped on the way back
+        gap, rot = _conservation(*args)[0]
+        assert np.abs(gap).max() < 1e-11 and np.abs(rot).max() > 1e-3
