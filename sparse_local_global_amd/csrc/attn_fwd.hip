@@ -66,6 +66,8 @@ struct State {
 // tiles skip the accumulator rescale.  The result is exact up to rounding for any
 // reference, since numerator and denominator share it.
 constexpr float kRescale = 8.0f;
+// The same bound as a sum of weights (the bf16 kernels test sums, not maxima).
+constexpr float kSumLimit = 256.0f;
 
 // One staged tile: scores, mask, online-softmax update and P.V.  Bit r of `live` says
 // whether tile row r is a real, unmasked key; all-ones tiles skip the masking.
@@ -539,28 +541,35 @@ void k_attn_fwd32d(FwdArgs a) {
         if (!((mine >> r) & 1u)) sc[i] = -INFINITY;
       }
     }
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mx *= c;
-    if (mx > st.m + kRescale) {
-      const float alpha = fast_exp2(st.m - mx);
-      st.m = mx;
-      st.l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt) st.o[dt] *= alpha;
-    }
-    const float mneg = -st.m;
+    // Exponentiate against the current reference maximum without looking for the tile's
+    // own: when no lane's sum over its 16 keys exceeds kSumLimit, no weight exceeds it
+    // either and the reference may stay (lazy rescaling, exact up to rounding since
+    // numerator and denominator share it).  Otherwise, and on the first live tile where
+    // no reference exists yet, the exact tile maximum becomes the reference.
+    bf16x8 pb[2];
     float ls = 0.f;
+    bool slow = __ballot(st.m == -INFINITY) != 0ull;
+    if (!slow) {
+      ls = exp_pack32(sc, c, st.m, pb);
+      slow = __ballot(!(ls <= kSumLimit)) != 0ull;
+    }
+    if (slow) {
+      float mx = sc[0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(sc[i], c, mneg));
-      sc[i] = p;
-      ls += p;
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= c;
+      if (mx > st.m) {
+        const float alpha = fast_exp2(st.m - mx);  // 0 while the reference is -inf (o, l are 0)
+        st.m = mx;
+        st.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DP / 32; ++dt) st.o[dt] *= alpha;
+      }
+      ls = exp_pack32(sc, c, st.m, pb);
     }
     st.l += ls;
-    accum32_frag(vfr, sc, st.o);
+    accum32_packed(vfr, pb, st.o);
   };
   // Two stages.  The compiler makes every LDS transpose load wait for all copies in
   // flight, so each step reads its V operands right after the wait for its own tile and

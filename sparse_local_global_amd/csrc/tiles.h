@@ -374,6 +374,34 @@ __device__ inline void accum32_frag(const RowsFrag32<DP>& v, const f32x16& p, f3
   }
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// p = exp2(c s - m) for the 16 slots of a 32x32 score block, rounded to bf16 into the B
+// operand of accum32 (pb[s] holds slots 8s .. 8s+7).  Returns the sum of the rounded
+// values (two per v_dot2 against (1, 1), fp32 accumulation): the weights the product
+// with V actually uses.
+__device__ inline float exp_pack32(const f32x16& s, float c, float m, bf16x8 (&pb)[2]) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bf16x2 q = {(bf16)fast_exp2(fmaf(s[2 * j], c, -m)), (bf16)fast_exp2(fmaf(s[2 * j + 1], c, -m))};
+    pb[j >> 2][2 * (j & 3)] = q[0];
+    pb[j >> 2][2 * (j & 3) + 1] = q[1];
+    sum = __builtin_amdgcn_fdot2_f32_bf16(q, one, sum, false);
+  }
+  return sum;
+}
+
+// accum32_frag with the B operand already packed by exp_pack32.
+template <int DP>
+__device__ inline void accum32_packed(const RowsFrag32<DP>& v, const bf16x8 (&pb)[2], f32x16 (&acc)[DP / 32]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.a[s][dt], pb[s], acc[dt], 0, 0, 0);
+}
+
 // ---- direct global -> LDS copies ------------------------------------------------------
 // buffer_load_dwordx4 ... lds writes the 16 bytes lane l loads to LDS address
 // M0 + 16 l (dword size: M0 + 4 l), and an out-of-range load writes zeros.  One wave
