@@ -486,18 +486,27 @@ void k_attn_fwd32d(FwdArgs a) {
   const bf16* vq = (const bf16*)a.vr + bh * N * DP;
   const bf16* kbq = (const bf16*)a.kbar + bh * a.nblkp * DP;
   const bf16* vbq = (const bf16*)a.vbar + bh * a.nblkp * DP;
+  const size_t bytes_loc = (size_t)N * DP * es, bytes_sum = (size_t)a.nblkp * DP * es;
+  // ONE_BLOCK: tiles are issued in order, so a cursor (entry of the neighbour list,
+  // 64-row tile within that block) replaces a division per tile
+  const int tpb = a.tiles_per_block;
+  int cur_entry = 0, cur_sub = 0;
   auto issue = [&](auto sg, int t) {
     FwdStage32<DP>& S = stage(sg);
     if constexpr (ONE_BLOCK) {
       // one contiguous run per tensor: select the (uniform) base pointers and build the
-      // buffer resources here, so they stay scalar
+      // buffer resources at one call site, so they stay scalar
       const bool loc = t < nlt;
       uint32_t row0 = (uint32_t)(t - nlt) * kTile;
       if (loc) {
-        const VirtualRows vr(sm.list, bvol, t * kTile);
-        row0 = (uint32_t)(vr.blk0 * bvol + vr.off0);
+        const int blk = __builtin_amdgcn_readfirstlane(sm.list[cur_entry]);
+        row0 = (uint32_t)(blk * bvol + cur_sub * kTile);
+        if (++cur_sub == tpb) {
+          cur_sub = 0;
+          ++cur_entry;
+        }
       }
-      const size_t bytes = (loc ? (size_t)N : (size_t)a.nblkp) * DP * es;
+      const size_t bytes = loc ? bytes_loc : bytes_sum;
       const Src ks(loc ? kq : kbq, bytes), vs(loc ? vq : vbq, bytes);
       dma.issue_at(ks, S.k, row0 * DP);
       dma.issue_at(vs, S.v, row0 * DP);
@@ -521,16 +530,22 @@ void k_attn_fwd32d(FwdArgs a) {
     const FwdStage32<DP>& S = stage(sg);
     uint64_t live;
     if (t < nlt) {
-      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
-      live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
-      if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+      if constexpr (ONE_BLOCK) {
+        live = a.holes ? occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), kTile) : ~0ull;
+      } else {
+        const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
+        live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+        if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+      }
     } else {
       const int ts = t - nlt, r0 = ts * kTile;
       const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
       const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
-    const uint32_t mine = (uint32_t)(live >> (32 * kh));  // this wave's 32 key rows
+    // this wave's 32 key rows; uniform, so the branches on it stay scalar
+    const uint32_t mine =
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)(kh ? (uint32_t)(live >> 32) : (uint32_t)live));
     if (mine == 0u) return;  // nothing live here, and m may still be -inf
     f32x16 sc;
     score32_rows(S.k, f, sc, col, half, kh);
