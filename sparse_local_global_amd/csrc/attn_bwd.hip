@@ -15,7 +15,7 @@
 // as the forward does, and no kernel writes a gradient for them.
 //
 // Kernels, in launch order (no atomics anywhere, so results are bitwise reproducible):
-//   bwd_pre      per block: delta, dO and lse (in log2 units) gathered to canonical order
+//   bwd_pre      per block: -delta, dO and lse (in log2 units) gathered to canonical order
 //   bwd_summary  summary-major: each workgroup owns 64 summaries of one (volume, head) and a
 //                chunk of query blocks; masks the summaries local to each query block and
 //                accumulates partial dKbar, dVbar (fp32) per chunk
@@ -39,7 +39,8 @@ namespace {
 struct BwdArgs {
   // forward intermediates and backward layouts (workspace, canonical order)
   const void* qrot; const void* krot; const void* vr; const void* kbar; const void* vbar;
-  void* doc; float* lsec; float* delta;   // lsec: lse * log2(e), canonical order
+  // lsec: lse * log2(e); ndelta: -<dO, O> (score products of dP accumulate onto it); canonical order
+  void* doc; float* lsec; float* ndelta;
   float* dkbar; float* dvbar; float* part_k; float* part_v;
   const float2* tab;
   // caller buffers (packed order)
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
       const int src = a.perm[(int64_t)b * N + kappa];
       float s = 0.f;
       for (int c = 0; c < nch; ++c) s += part[tid * nch + c];
-      a.delta[bh * N + kappa] = s;
+      a.ndelta[bh * N + kappa] = -s;
       // log2 units; +inf for an empty slot makes every probability of that row 0
       a.lsec[bh * N + kappa] = src >= 0 ? a.lse[bh * a.Nmax + src] * kLog2e : INFINITY;
     }
@@ -170,7 +171,7 @@ __device__ inline void write_rows(const BwdArgs& a, const float* st, int sts, in
 template <typename T, int DP>
 struct SumSmem {
   RowTile<T, DP> q, g;
-  float lse[kTile], delta[kTile];
+  float lse[kTile], ndelta[kTile];
 };
 
 template <typename T, int DP, bool ONE_BLOCK>
@@ -211,7 +212,7 @@ void k_bwd_summary(BwdArgs a) {
   const int total = (q_end - q_begin) * tpb;
   struct Stage {
     RowRegs<T, DP> q, g;
-    float lse2, delta;  // of tile row tid (tid < 64)
+    float lse2, ndelta;  // of tile row tid (tid < 64)
   } st0, st1;
   auto fetch = [&](Stage& S, int t) {
     const int qb = q_begin + t / tpb, qs = t - (t / tpb) * tpb;
@@ -225,7 +226,7 @@ void k_bwd_summary(BwdArgs a) {
     }
     if (tid < kTile) {
       S.lse2 = tid < nrow ? a.lsec[bh * N + row0 + tid] : INFINITY;
-      S.delta = tid < nrow ? a.delta[bh * N + row0 + tid] : 0.f;
+      S.ndelta = tid < nrow ? a.ndelta[bh * N + row0 + tid] : 0.f;
     }
   };
   auto store = [&](const Stage& S) {
@@ -233,7 +234,7 @@ void k_bwd_summary(BwdArgs a) {
     S.g.store(sm.g);
     if (tid < kTile) {
       sm.lse[tid] = S.lse2;
-      sm.delta[tid] = S.delta;
+      sm.ndelta[tid] = S.ndelta;
     }
   };
   auto compute = [&](int t) {
@@ -243,7 +244,10 @@ void k_bwd_summary(BwdArgs a) {
     const bool masked = sid >= a.nblk || cheb <= a.radius;
     f32x4 s[4], dp[4];
     score(sm.q, kf, s, col, grp);
-    score(sm.g, vf, dp, col, grp);
+    // dp = <dO, V> - delta: the products accumulate onto -delta of rows 16mt + 4grp + i
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) dp[mt] = *(const f32x4*)&sm.ndelta[16 * mt + 4 * grp];
+    score_acc(sm.g, vf, dp, col, grp);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -252,7 +256,7 @@ void k_bwd_summary(BwdArgs a) {
         float p = fast_exp2(fmaf(s[mt][i], c, -sm.lse[r]));
         if (masked) p = 0.f;
         s[mt][i] = p;
-        dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
+        dp[mt][i] = p * dp[mt][i];
       }
     }
     accum(sm.g, s, dv, col, grp);
@@ -291,7 +295,7 @@ struct LocSmem {
     } t;
     float st[kTile][DP + 1];
   } u;
-  float lse[kTile], delta[kTile];
+  float lse[kTile], ndelta[kTile];
   int list[kMaxSlots];
   int nloc;
   int src[kTile], rel[kTile * 3];
@@ -331,7 +335,7 @@ void k_bwd_local(BwdArgs a) {
   const int ntiles = (nq + kTile - 1) / kTile;
   struct Stage {
     RowRegs<T, DP> q, g;
-    float lse2, delta;  // of tile row tid (tid < 64)
+    float lse2, ndelta;  // of tile row tid (tid < 64)
   } st0, st1;
   auto fetch = [&](Stage& S, int t) {
     const int j0 = t * kTile;
@@ -347,11 +351,11 @@ void k_bwd_local(BwdArgs a) {
     }
     if (tid < kTile) {
       S.lse2 = INFINITY;   // padding rows: P = 0
-      S.delta = 0.f;
+      S.ndelta = 0.f;
       if (tid < valid) {
         const int row = vr.row(tid);
         S.lse2 = a.lsec[bh * N + row];
-        S.delta = a.delta[bh * N + row];
+        S.ndelta = a.ndelta[bh * N + row];
       }
     }
   };
@@ -360,13 +364,16 @@ void k_bwd_local(BwdArgs a) {
     S.g.store(sm.u.t.g);
     if (tid < kTile) {
       sm.lse[tid] = S.lse2;
-      sm.delta[tid] = S.delta;
+      sm.ndelta[tid] = S.ndelta;
     }
   };
   auto compute = [&](int) {
     f32x4 s[4], dp[4];
     score(sm.u.t.q, kf, s, col, grp);
-    score(sm.u.t.g, vf, dp, col, grp);
+    // dp = <dO, V> - delta: the products accumulate onto -delta of rows 16mt + 4grp + i
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) dp[mt] = *(const f32x4*)&sm.ndelta[16 * mt + 4 * grp];
+    score_acc(sm.u.t.g, vf, dp, col, grp);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -374,7 +381,7 @@ void k_bwd_local(BwdArgs a) {
         const int r = 16 * mt + 4 * grp + i;
         const float p = fast_exp2(fmaf(s[mt][i], c, -sm.lse[r]));   // lse = +inf -> 0
         s[mt][i] = p;
-        dp[mt][i] = p * (dp[mt][i] - sm.delta[r]);
+        dp[mt][i] = p * dp[mt][i];
       }
     }
     accum(sm.u.t.g, s, dv, col, grp);
@@ -416,7 +423,7 @@ void k_bwd_local(BwdArgs a) {
 // query-row half qh = wave >> 1 of every query tile; the two query halves' partial
 // dK~, dV are summed through LDS before the epilogue.  v_mfma_f32_32x32x16_bf16 halves
 // the LDS reads per multiply against 16-column waves, and the copies (query tile, dO
-// tile, lse, delta) hold no registers, so three LDS stages keep two tiles in flight.
+// tile, lse, -delta) hold no registers, so three LDS stages keep two tiles in flight.
 // Rows past the end of the last tile arrive as zeros: Q = dO = 0 there, so their
 // probabilities multiply zero rows and add nothing.
 // ---------------------------------------------------------------------------------
@@ -425,7 +432,7 @@ constexpr int kLdsStages = 3;
 template <int DP>
 struct LocStage32 {
   RowTile<bf16, DP> q, g;
-  float lse2[kTile], delta[kTile];
+  float lse2[kTile], ndelta[kTile];
 };
 
 template <int DP>
@@ -532,7 +539,7 @@ __device__ inline void local32_epilogue96(const BwdArgs& a, f32x16 (&dk)[3], f32
           bf16x4{(bf16)acc[dt][4 * jj], (bf16)acc[dt][4 * jj + 1], (bf16)acc[dt][4 * jj + 2], (bf16)acc[dt][4 * jj + 3]};
 }
 
-// Direct copy of lse2 / delta for tile rows 16 w .. 16 w + 15 (lanes 0..15 of wave w).
+// Direct copy of lse2 / -delta for tile rows 16 w .. 16 w + 15 (lanes 0..15 of wave w).
 __device__ inline void issue_rows16(const Src& src, float* dst16, uint32_t byte_off) {
   if ((threadIdx.x & 63) < 16)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_void*)dst16, 4, byte_off, 0, 0, 0);
@@ -573,7 +580,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const Src qrot((const bf16*)a.qrot + bh * N * DP, slice);
   const Src doc((const bf16*)a.doc + bh * N * DP, slice);
   const Src lsec(a.lsec + bh * N, (size_t)N * sizeof(float));
-  const Src dlt(a.delta + bh * N, (size_t)N * sizeof(float));
+  const Src dlt(a.ndelta + bh * N, (size_t)N * sizeof(float));
   const float c = a.scale_log2;
   const int nq = nloc * bvol;
   const int ntiles = (nq + kTile - 1) / kTile;
@@ -594,30 +601,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       dma.issue_at(qrot, S.q, (uint32_t)row0 * DP);
       dma.issue_at(doc, S.g, (uint32_t)row0 * DP);
       issue_rows16(lsec, &S.lse2[16 * w], (uint32_t)(row0 + r) * 4u);
-      issue_rows16(dlt, &S.delta[16 * w], (uint32_t)(row0 + r) * 4u);
+      issue_rows16(dlt, &S.ndelta[16 * w], (uint32_t)(row0 + r) * 4u);
     } else {
       const int valid = nq - j0 < kTile ? nq - j0 : kTile;
       dma.issue(qrot, S.q, valid, [&](int rr) { return vr.row(rr) * DP; });
       dma.issue(doc, S.g, valid, [&](int rr) { return vr.row(rr) * DP; });
       const uint32_t off = r < valid ? (uint32_t)vr.row(r) * 4u : 0x80000000u;
       issue_rows16(lsec, &S.lse2[16 * w], off);
-      issue_rows16(dlt, &S.delta[16 * w], off);
+      issue_rows16(dlt, &S.ndelta[16 * w], off);
     }
   };
   auto compute = [&](auto st, int) {
     const LocStage32<DP>& S = stage(st);
-    f32x16 s, dp;
-    score32_pair(S.q, kf, s, S.g, vf, dp, col, half, qh);
+    // dp = <dO, V> - delta: the products accumulate onto -delta; slots 4j .. 4j+3 are
+    // rows 32qh + 8j + 4half + e
+    f32x16 s, dp, nd;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // slots 4j .. 4j+3: rows 32qh + 8j + 4half + e
+      const f32x4 d4 = *(const f32x4*)&S.ndelta[32 * qh + 8 * j + 4 * half];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nd[4 * j + e] = d4[e];
+    }
+    score32_pair(S.q, kf, s, S.g, vf, dp, col, half, qh, nd);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       const f32x4 l4 = *(const f32x4*)&S.lse2[32 * qh + 8 * j + 4 * half];
-      const f32x4 d4 = *(const f32x4*)&S.delta[32 * qh + 8 * j + 4 * half];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float p = fast_exp2(fmaf(s[4 * j + e], c, -l4[e]));
         s[4 * j + e] = p;
-        dp[4 * j + e] = p * (dp[4 * j + e] - d4[e]);
+        dp[4 * j + e] = p * dp[4 * j + e];
       }
     }
     accum32_rows(S.g, s, dv, lane, half, qh);
@@ -709,11 +722,14 @@ struct DqSmem {
 // Bit r of `live` says whether tile row r is a real, unmasked key.
 template <typename T, int DP>
 __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf, const ColFrag<T, DP>& gf,
-                               f32x4 (&dq)[DP / 16], float lse2, float delta, float c, int col, int grp,
+                               f32x4 (&dq)[DP / 16], float lse2, float ndelta, float c, int col, int grp,
                                uint64_t live) {
   f32x4 s[4], dp[4];
   score(sm.u.t.k, qf, s, col, grp);
-  score(sm.u.t.v, gf, dp, col, grp);
+  // dp = <dO, V> - delta: the products accumulate onto -delta (one value per lane's query)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) dp[mt] = f32x4{ndelta, ndelta, ndelta, ndelta};
+  score_acc(sm.u.t.v, gf, dp, col, grp);
   if (live != ~0ull) {
     const uint64_t bits = live >> (4 * grp);  // row 16mt + 4grp + i -> bit 16mt + i
 #pragma unroll
@@ -729,7 +745,7 @@ __device__ inline void dq_step(const DqSmem<T, DP>& sm, const ColFrag<T, DP>& qf
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float p = fast_exp2(fmaf(s[mt][i], c, -lse2));
-      dp[mt][i] = p * (dp[mt][i] - delta);
+      dp[mt][i] = p * dp[mt][i];
     }
   }
   accum(sm.u.t.k, dp, dq, col, grp);
@@ -815,7 +831,7 @@ void k_bwd_dq(BwdArgs a) {
   qf.load((const T*)a.qrot + (bh * N + qrow0 + qloc) * DP, qok, grp);
   gf.load((const T*)a.doc + (bh * N + qrow0 + qloc) * DP, qok, grp);
   const float lse2 = qok ? a.lsec[bh * N + qrow0 + qloc] : INFINITY;
-  const float delta = qok ? a.delta[bh * N + qrow0 + qloc] : 0.f;
+  const float ndelta = qok ? a.ndelta[bh * N + qrow0 + qloc] : 0.f;
 
   const int mask_words = a.nblkp / 32;
   // summaries: empty blocks start masked (as in the forward), the local blocks are added below
@@ -876,7 +892,7 @@ void k_bwd_dq(BwdArgs a) {
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
     if (live == 0ull) return;
-    dq_step(sm, qf, gf, dq, lse2, delta, c, col, grp, live);
+    dq_step(sm, qf, gf, dq, lse2, ndelta, c, col, grp, live);
   };
   pipeline2(total, st0, st1, fetch, store, compute);
   if constexpr (DP == 96) {
@@ -966,7 +982,7 @@ pack3d_status launch_attn_bwd(const Dims& d, const pack3d_index* ix, const pack3
                               char* ws, const Workspace& w, hipStream_t s) {
   BwdArgs a;
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
-  a.doc = ws + w.doc; a.lsec = (float*)(ws + w.lsec); a.delta = (float*)(ws + w.delta);
+  a.doc = ws + w.doc; a.lsec = (float*)(ws + w.lsec); a.ndelta = (float*)(ws + w.delta);
   a.dkbar = (float*)(ws + w.dkbar); a.dvbar = (float*)(ws + w.dvbar);
   a.part_k = (float*)(ws + w.part_k); a.part_v = (float*)(ws + w.part_v);
   a.tab = (const float2*)(ws + w.rope);

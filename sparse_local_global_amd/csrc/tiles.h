@@ -109,13 +109,14 @@ template <int DP> struct ColFrag<float, DP> {
   }
 };
 
+// score_acc adds the scores onto the values s holds (an offset per element); score
+// starts from zero.
 template <int DP>
-__device__ inline void score(const RowTile<bf16, DP>& t, const ColFrag<bf16, DP>& f, f32x4 (&s)[4], int col, int grp) {
+__device__ inline void score_acc(const RowTile<bf16, DP>& t, const ColFrag<bf16, DP>& f, f32x4 (&s)[4], int col,
+                                 int grp) {
   using G = TileGeom<bf16, DP>;
   const bf16* b0 = t.x + G::base(col, grp);  // row 16mt + col, chunk 4k + grp
   // k outer, row tile inner: the four accumulation chains interleave
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < DP / 32; ++k) {
 #pragma unroll
@@ -127,11 +128,12 @@ __device__ inline void score(const RowTile<bf16, DP>& t, const ColFrag<bf16, DP>
 }
 
 template <int DP>
-__device__ inline void score(const RowTile<float, DP>& t, const ColFrag<float, DP>& f, f32x4 (&s)[4], int col, int grp) {
+__device__ inline void score_acc(const RowTile<float, DP>& t, const ColFrag<float, DP>& f, f32x4 (&s)[4], int col,
+                                 int grp) {
   using G = TileGeom<float, DP>;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = s[mt];
 #pragma unroll
     for (int k = 0; k < DP / 4; k += 4) {
       const f32x4 a = *(const f32x4*)&t.x[(16 * mt + col) * G::RS + grp * (DP / 4) + k];
@@ -140,6 +142,13 @@ __device__ inline void score(const RowTile<float, DP>& t, const ColFrag<float, D
     }
     s[mt] = acc;
   }
+}
+
+template <typename T, int DP>
+__device__ inline void score(const RowTile<T, DP>& t, const ColFrag<T, DP>& f, f32x4 (&s)[4], int col, int grp) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  score_acc(t, f, s, col, grp);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -276,15 +285,16 @@ __device__ inline void accum32(const RowTile<bf16, DP>& t, const f32x16 (&p)[2],
 // One 32-row block (rows 32mt .. 32mt+31) of two independent score tiles at once
 // (the two accumulation chains interleave): s1 from t1 and f1, s2 from t2 and f2,
 // slot i = row 32mt + 8(i/4) + 4h + i%4 against column (lane & 31).
+// s2 starts from init2 (an offset per element), s1 from zero.
 template <int DP>
 __device__ inline void score32_pair(const RowTile<bf16, DP>& t1, const ColFrag32<DP>& f1, f32x16& s1,
                                     const RowTile<bf16, DP>& t2, const ColFrag32<DP>& f2, f32x16& s2, int col,
-                                    int half, int mt) {
+                                    int half, int mt, const f32x16& init2 = f32x16{}) {
   using G = TileGeom<bf16, DP>;
   const int be = G::base(col & 15, half) + G::off(col & 16, 0);
   const int bo = G::base(col & 15, 2 + half) + G::off(col & 16, 0);
   s1 = f32x16{};
-  s2 = f32x16{};
+  s2 = init2;
 #pragma unroll
   for (int k = 0; k < DP / 16; ++k) {
     const int o = (k & 1 ? bo : be) + G::off(32 * mt, 4 * (k >> 1));
