@@ -167,3 +167,33 @@ def test_forward_errors():
     with pytest.raises(p3.Pack3DError) as e:
         p3.forward(ix, x["q"].half(), x["k"].half(), x["v"].half(), x["coords"])
     assert e.value.status == p3.E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("scale", [3.0, 6.0])
+def test_large_logits_exact_operands(scale):
+    """Logits spread over tens to hundreds of units (lse up to about 190 at scale 6), so later
+    tiles overtake the running reference maximum by far more than 2^8 and the forward takes
+    its exact-maximum rescaling branch mid-stream, not only on the first tile.  Position mode
+    "none" keeps the rotated operands equal to the bf16 inputs, so scores are exact products
+    on both sides and the bf16 rounding of the weights is the only approximation.  Outputs and
+    gradients grow with the inputs (|o| reaches about 8 at scale 3, where half a bf16 ulp is
+    already 0.03), so they are held to 2e-2 of their largest reference magnitude; lse keeps
+    the absolute bound."""
+    w = si.small_workload(grid=(8, 8, 16), block=(4, 4, 4), radius=1, heads=2, head_dim=96, packing="random",
+                          seed=72, input_scale=scale)
+    dtype = torch.bfloat16
+    say(f"large logits scale={scale}")
+    x = si.make_inputs(w, dtype, with_grad=True)
+    xd = to_dev(x)
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    out, lse = p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], position_mode="none")
+    grads = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], position_mode="none")
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], x["coords"], w.block, w.radius, position_mode="none")
+    assert max_err(out, o_ref) < TOL[dtype] * max(1.0, float(np.abs(o_ref).max()))
+    assert max_err(lse, l_ref) < TOL[dtype]
+    assert float(np.nanmax(l_ref)) > 15.0 * scale
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius, position_mode="none")
+    for name, g, rr in zip(("dq", "dk", "dv"), grads, ref):
+        err = max_err(g, rr)
+        assert err < TOL[dtype] * max(1.0, float(np.abs(rr).max())), (name, err, float(np.abs(rr).max()))
