@@ -25,7 +25,7 @@
 namespace pack3d {
 namespace {
 
-constexpr int kChunk = 64;  // tokens staged in LDS at a time
+constexpr int kChunk = 32;  // tokens staged in LDS at a time (32: six workgroups per CU fit)
 
 __global__ void k_rope_table(float2* tab, int rows, int half, int gw, double base) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   for (int hh = 0; hh < a.heads_per_group; ++hh) {
     const int h = h0 + hh;
     const int64_t bh = (int64_t)b * H + h;
-    float ksum = 0.f, vsum = 0.f;   // column tid < Dp
+    float csum = 0.f;   // K~ column tid (tid < Dp) or V column tid - Dp (tid < 2 Dp)
     for (int ch = 0; ch < nchunk; ++ch) {
       const int t0 = ch * ntok;
       // rotate q and k
@@ -178,28 +178,25 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         }
       }
       __syncthreads();
-      if (tid < Dp) {
-        float ks = 0.f, vs = 0.f;
-        for (int t = 0; t < ntok; ++t) {
-          ks += kl[t * ls + tid];
-          vs += vl[t * ls + tid];
-        }
-        ksum += ks;
-        vsum += vs;
+      // column sums over the chunk: threads 0 .. Dp-1 sum K~ columns, Dp .. 2Dp-1 V columns
+      if (tid < 2 * Dp) {
+        const float* col = tid < Dp ? kl + tid : vl + (tid - Dp);
+        float cs = 0.f;
+        for (int t = 0; t < ntok; ++t) cs += col[t * ls];
+        csum += cs;
       }
       __syncthreads();
     }
-    if (tid < Dp) {
+    if (tid < 2 * Dp) {
       // mean over the tokens present (|b| on a full grid); an empty block's sums are 0
       const int cnt = a.holes ? a.count[(int64_t)b * a.nblk + blk] : bvol;
       const float inv = cnt > 0 ? 1.0f / (float)cnt : 0.f;
-      ((T*)a.kbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(ksum * inv);
-      ((T*)a.vbar)[(bh * a.nblkp + blk) * Dp + tid] = from_f<T>(vsum * inv);
+      T* bar = tid < Dp ? (T*)a.kbar : (T*)a.vbar;
+      const int c = tid < Dp ? tid : tid - Dp;
+      bar[(bh * a.nblkp + blk) * Dp + c] = from_f<T>(csum * inv);
       // zero the padding summaries nblk .. nblkp (there may be more of them than blocks)
-      for (int pad_blk = a.nblk + blk; pad_blk < a.nblkp; pad_blk += a.nblk) {
-        ((T*)a.kbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
-        ((T*)a.vbar)[(bh * a.nblkp + pad_blk) * Dp + tid] = from_f<T>(0.f);
-      }
+      for (int pad_blk = a.nblk + blk; pad_blk < a.nblkp; pad_blk += a.nblk)
+        bar[(bh * a.nblkp + pad_blk) * Dp + c] = from_f<T>(0.f);
     }
   }
 }
