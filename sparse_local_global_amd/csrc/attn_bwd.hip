@@ -703,6 +703,140 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------------------------
+// bwd_summary for bf16 with 32 summary columns per wave (Dp 32, 96), fed by direct LDS
+// copies as bwd_local32 is: workgroup = (64 summaries, head, volume x query chunk), four
+// waves = summary half kh x query-row half qh of every query tile.  A summary's
+// probability is zero for the query blocks it is local to (and for the padding
+// summaries past the last block).  The two query halves' partial dKbar~, dVbar are added
+// through LDS and written as the chunk's partial rows, as bwd_summary does.
+// ---------------------------------------------------------------------------------
+template <int DP, bool ONE_BLOCK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_summary32(BwdArgs a) {
+  // one LDS object per stage; the epilogue reuses stages 0 / 1 for query half 1's partial
+  // sums of summary half 0 / 1 ([slot][lane] float4s)
+  __shared__ LocStage32<DP> s0, s1, s2;
+  static_assert(sizeof(f32x4) * DP / 32 * 8 * 64 <= sizeof(LocStage32<DP>), "partials fit a stage");
+  // 1-D grid over (summary tile, chunk, head, volume), summary tile fastest
+  const int nst = a.nblkp / kTile;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int r0 = (L % nst) * kTile, chunk = (L / nst) % a.chunks;
+  const int h = (L / nst / a.chunks) % a.H, b = L / nst / a.chunks / a.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int N = a.NC, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int sid = r0 + 32 * kh + col;  // this lane's summary (block id); padding rows are zero
+  ColFrag32<DP> kf, vf;
+  kf.load((const bf16*)a.kbar + (bh * a.nblkp + sid) * DP, true, half);
+  vf.load((const bf16*)a.vbar + (bh * a.nblkp + sid) * DP, true, half);
+  const int32_t* g = a.geom + b * G_FIELDS;
+  // the volume's block grid covers its bounding box: ceil(extent / b) blocks per axis
+  const int nby = (g[G_EY] + a.by - 1) / a.by, nbx = (g[G_EX] + a.bx - 1) / a.bx;
+  const int sz = sid / (nby * nbx), sy = (sid / nbx) % nby, sx = sid % nbx;
+  f32x16 dk[DP / 32], dv[DP / 32];
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) dk[dt] = dv[dt] = f32x16{};
+
+  const int q_begin = (int)((int64_t)chunk * a.nblk / a.chunks);
+  const int q_end = (int)((int64_t)(chunk + 1) * a.nblk / a.chunks);
+  const int nrow = bvol < kTile ? bvol : kTile;
+  const int tpb = a.tiles_per_block;
+  const size_t slice = (size_t)N * DP * sizeof(bf16);
+  const Src qrot((const bf16*)a.qrot + bh * N * DP, slice);
+  const Src doc((const bf16*)a.doc + bh * N * DP, slice);
+  const Src lsec(a.lsec + bh * N, (size_t)N * sizeof(float));
+  const Src dlt(a.ndelta + bh * N, (size_t)N * sizeof(float));
+  const float c = a.scale_log2;
+  // tile t = (query block q_begin + t / tpb, sub-tile t % tpb); rows past a block of fewer
+  // than 64 tokens arrive as zeros (Q = dO = 0 there, so they add nothing)
+  const int ntiles = (q_end - q_begin) * tpb;
+  using Dma = TileDma<DP, kThreads>;
+  const Dma dma;
+  auto stage = [&](auto st) -> LocStage32<DP>& {
+    if constexpr (decltype(st)::value == 0) return s0;
+    else if constexpr (decltype(st)::value == 1) return s1;
+    else return s2;
+  };
+  auto issue = [&](auto st, int t) {
+    LocStage32<DP>& S = stage(st);
+    const int qb = q_begin + t / tpb, qs = t - (t / tpb) * tpb;
+    const int row0 = qb * bvol + qs * kTile;
+    const int w = wave_id(), r = 16 * w + (lane & 15);
+    // (issue_at in this generic lambda costs another kernel's host-side stub, see
+    // bwd_local32; the row form serves both layouts)
+    dma.issue(qrot, S.q, nrow, [&](int rr) { return (row0 + rr) * DP; });
+    dma.issue(doc, S.g, nrow, [&](int rr) { return (row0 + rr) * DP; });
+    const uint32_t off = r < nrow ? (uint32_t)(row0 + r) * 4u : 0x80000000u;
+    issue_rows16(lsec, &S.lse2[16 * w], off);
+    issue_rows16(dlt, &S.ndelta[16 * w], off);
+  };
+  auto compute = [&](auto st, int t) {
+    const LocStage32<DP>& S = stage(st);
+    const int qb = q_begin + t / tpb;
+    const int qz = qb / (nby * nbx), qy = (qb / nbx) % nby, qx = qb % nbx;
+    const int cheb = max(max(abs(qz - sz), abs(qy - sy)), abs(qx - sx));
+    const bool masked = sid >= a.nblk || cheb <= a.radius;  // per lane: this summary column
+    // dp = <dO, Vbar> - delta: the products accumulate onto -delta; slots 4j .. 4j+3 are
+    // rows 32qh + 8j + 4half + e
+    f32x16 s, dp, nd;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 d4 = *(const f32x4*)&S.ndelta[32 * qh + 8 * j + 4 * half];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nd[4 * j + e] = d4[e];
+    }
+    score32_pair(S.q, kf, s, S.g, vf, dp, col, half, qh, nd);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l4 = *(const f32x4*)&S.lse2[32 * qh + 8 * j + 4 * half];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p = fast_exp2(fmaf(s[4 * j + e], c, -l4[e]));
+        if (masked) p = 0.f;
+        s[4 * j + e] = p;
+        dp[4 * j + e] = p * dp[4 * j + e];
+      }
+    }
+    accum32_rows(S.g, s, dv, lane, half, qh);
+    accum32_rows(S.q, dp, dk, lane, half, qh);
+  };
+  pipeline_lds<kLdsStages, 2 * Dma::ROUNDS + 2>(ntiles, issue, compute);
+  __syncthreads();  // the partial sums below overlay the stages
+
+  constexpr int NDT = DP / 32;
+  f32x4* part = (f32x4*)(kh == 0 ? (void*)&s0 : (void*)&s1);
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        part[(4 * dt + q) * 64 + lane] = f32x4{dk[dt][4 * q], dk[dt][4 * q + 1], dk[dt][4 * q + 2], dk[dt][4 * q + 3]};
+        part[(4 * NDT + 4 * dt + q) * 64 + lane] =
+            f32x4{dv[dt][4 * q], dv[dt][4 * q + 1], dv[dt][4 * q + 2], dv[dt][4 * q + 3]};
+      }
+  }
+  __syncthreads();
+  if (qh == 1) return;
+  // value of dim 32dt + 8jj + 4half + e is slot 4jj + e of block dt
+  const int64_t base = (((int64_t)chunk * a.B * a.H + bh) * a.nblkp + sid) * DP;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 pk = part[(4 * dt + jj) * 64 + lane], pv = part[(4 * NDT + 4 * dt + jj) * 64 + lane];
+      f32x4 ok, ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ok[e] = (dk[dt][4 * jj + e] + pk[e]) * a.scale;
+        ov[e] = dv[dt][4 * jj + e] + pv[e];
+      }
+      *(f32x4*)(a.part_k + base + 32 * dt + 8 * jj + 4 * half) = ok;
+      *(f32x4*)(a.part_v + base + 32 * dt + 8 * jj + 4 * half) = ov;
+    }
+}
+
+// ---------------------------------------------------------------------------------
 // bwd_dq: workgroup = (64 queries of one block, head, volume)
 // ---------------------------------------------------------------------------------
 template <typename T, int DP>
@@ -917,8 +1051,12 @@ pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   if (a.with_summaries) {
     {
       ProfileScope prof("bwd_summary", s);
-      hipLaunchKernelGGL((k_bwd_summary<T, DP, ONE_BLOCK>), dim3(d.nblkp / kTile * a.chunks * d.H * d.B),
-                         dim3(kThreads), 0, s, a);
+      const dim3 grid(d.nblkp / kTile * a.chunks * d.H * d.B);
+      // 32-column waves with direct LDS copies for bf16 where rows need no padding
+      if constexpr (sizeof(T) == 2 && (DP == 32 || DP == 96))
+        hipLaunchKernelGGL((k_bwd_summary32<DP, ONE_BLOCK>), grid, dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_bwd_summary<T, DP, ONE_BLOCK>), grid, dim3(kThreads), 0, s, a);
     }
     const int64_t n = (int64_t)d.B * d.H * d.nblkp * d.Dp;
     ProfileScope prof("bwd_reduce", s);
