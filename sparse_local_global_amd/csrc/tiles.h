@@ -371,19 +371,6 @@ __device__ inline void read_rows32(const RowTile<bf16, DP>& t, RowsFrag32<DP>& v
     }
 }
 
-// accum32_rows with the operands read beforehand by read_rows32.
-template <int DP>
-__device__ inline void accum32_frag(const RowsFrag32<DP>& v, const f32x16& p, f32x16 (&acc)[DP / 32]) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    bf16x8 b;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = (bf16)p[8 * s + e];
-#pragma unroll
-    for (int dt = 0; dt < DP / 32; ++dt) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.a[s][dt], b, acc[dt], 0, 0, 0);
-  }
-}
-
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // p = exp2(c s - m) for the 16 slots of a 32x32 score block, rounded to bf16 into the B
@@ -403,7 +390,8 @@ __device__ inline float exp_pack32(const f32x16& s, float c, float m, bf16x8 (&p
   return sum;
 }
 
-// accum32_frag with the B operand already packed by exp_pack32.
+// acc[dt] += V^T P with the A operands read beforehand by read_rows32 and the B operand
+// packed by exp_pack32.
 template <int DP>
 __device__ inline void accum32_packed(const RowsFrag32<DP>& v, const bf16x8 (&pb)[2], f32x16 (&acc)[DP / 32]) {
 #pragma unroll
