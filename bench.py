@@ -218,7 +218,7 @@ def main(argv=None) -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); the operator "
-              f"is benchmarked per GPU and this build has no multi-GPU path.", file=sys.stderr)
+              f"is benchmarked per GPU and the library has no multi-GPU path.", file=sys.stderr)
         return 2
 
     import torch
