@@ -175,22 +175,35 @@ def block_step(w, coords, steps: int, warmup: int) -> dict:
 
 
 def cpu_baseline(w, x, sample_blocks: int) -> dict:
-    """The fp64 oracle on the host cores: all heads of the first `sample_blocks` query blocks of each volume."""
+    """The fp64 oracle on the host cores, in the metric's unit (tokens/s of a forward + backward
+    step), from two bounded samples of the same workload: the forward of all heads of the first
+    `sample_blocks` query blocks of each volume, and the backward (every gradient) of volume 0,
+    head 0.  Each sample gives a token rate for all heads; the step rate combines the two."""
     import oracle  # test infrastructure, used only for this reported baseline
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:  # threadpoolctl missing: numpy's BLAS uses every core
         cores = os.cpu_count() or 1
+    bvol = int(w.block[0] * w.block[1] * w.block[2])
     blocks = list(range(sample_blocks))
     t0 = time.perf_counter()
     oracle.forward(x["q"], x["k"], x["v"], x["coords"], w.block, w.radius, query_blocks=blocks)
-    dt = time.perf_counter() - t0
-    tokens = w.batch * sample_blocks * int(w.block[0] * w.block[1] * w.block[2])
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"forward only: {sample_blocks} of {w.tokens // (w.block[0] * w.block[1] * w.block[2])} "
-                      f"query blocks per volume, all {w.heads} heads, both volumes ({tokens} query tokens), "
-                      f"fp64 NumPy, {dt:.1f} s including the whole-volume RoPE and pooling"}
+    dt_f = time.perf_counter() - t0
+    fwd_tokens = w.batch * sample_blocks * bvol
+    fwd_rate = fwd_tokens / dt_f
+    t0 = time.perf_counter()
+    oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius, volumes=[0], heads=[0])
+    dt_b = time.perf_counter() - t0
+    bwd_rate = w.tokens / w.heads / dt_b   # one head of one volume: 1/H of that volume's token work
+    step_rate = 1.0 / (1.0 / fwd_rate + 1.0 / bwd_rate)
+    return {"value": step_rate, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"forward: {sample_blocks} of {w.tokens // bvol} query blocks per volume, all {w.heads} "
+                      f"heads, both volumes ({fwd_tokens} query tokens, {dt_f:.1f} s including the whole-volume "
+                      f"RoPE and pooling); backward: every gradient of volume 0, head 0 of {w.heads} "
+                      f"({w.tokens} tokens, {dt_b:.1f} s); value = 1 / (1 / forward rate + 1 / backward rate), "
+                      f"fp64 NumPy",
+            "forward_tokens_per_s": fwd_rate, "backward_tokens_per_s": bwd_rate}
 
 
 def main(argv=None) -> int:
@@ -398,7 +411,8 @@ def main(argv=None) -> int:
         result["roofline"]["frac_of_gemm_ceiling"] = dk["tflops"] / g["tflops"]
         result["attn_fwd_frac_of_gemm_ceiling"] = result["attn_fwd_tflops"] / g["tflops"]
     if not args.no_cpu_baseline:
-        log(f"bench: timing the fp64 oracle on {args.cpu_sample_blocks} query blocks per volume")
+        log(f"bench: timing the fp64 oracle (forward sample of {args.cpu_sample_blocks} query blocks per "
+            f"volume, backward of one volume and head)")
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_blocks)
     print(json.dumps(result), flush=True)
     return 0
