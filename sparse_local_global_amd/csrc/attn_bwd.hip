@@ -839,6 +839,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ---------------------------------------------------------------------------------
 // bwd_dq: workgroup = (64 queries of one block, head, volume)
 // ---------------------------------------------------------------------------------
+// Local key tiles whose live-row masks bwd_dq precomputes when slots can be empty.
+constexpr int kDqLiveTiles = 512;
+
 template <typename T, int DP>
 struct DqSmem {
   union {
@@ -849,6 +852,7 @@ struct DqSmem {
   } u;
   int list[kMaxSlots];
   uint32_t mask[kMaxBlocks / 32];
+  uint64_t live[kDqLiveTiles];  // local tile t: bit r = key row r holds a token (empty slots only)
   int nloc;
   int src[kTile], rel[kTile * 3];
 };
@@ -987,6 +991,18 @@ void k_bwd_dq(BwdArgs a) {
   const int nkeys = nloc * bvol;
   const int nlt = (nkeys + kTile - 1) / kTile;
   const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
+  // With empty slots the local tiles' live-row masks come from the occupancy bits.  They are
+  // taken here, one tile per wave at a time, because a load of occupancy words inside the
+  // pipeline would also wait for the tile loads in flight.
+  const bool live_table = a.holes && nlt <= kDqLiveTiles;
+  if (live_table) {
+    for (int t = wave; t < nlt; t += kThreads / 64) {
+      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
+      const uint64_t lv = occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+      if (lane == 0) sm.live[t] = lv;
+    }
+    __syncthreads();
+  }
   struct Stage {
     RowRegs<T, DP> k, v;
   } st0, st1;
@@ -1018,7 +1034,8 @@ void k_bwd_dq(BwdArgs a) {
     if (t < nlt) {
       const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
       live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
-      if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+      if (live_table) live &= sm.live[t];
+      else if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
     } else {
       const int ts = t - nlt, r0 = ts * kTile;
       const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;

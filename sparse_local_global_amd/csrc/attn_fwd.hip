@@ -526,8 +526,10 @@ void k_attn_fwd32d(FwdArgs a) {
       dma.issue(vbar, S.v, kTile, [&](int r) { return (r0 + r) * DP; });
     }
   };
-  auto compute = [&](auto sg, int t, const RowsFrag32<DP>& vfr) {
-    const FwdStage32<DP>& S = stage(sg);
+  // This wave's live key rows of tile t (bit r: row 32kh + r).  It runs before the next
+  // tile's copies are issued: with empty slots it loads occupancy words, and a wait for
+  // those would otherwise also wait for the copies.
+  auto live_rows = [&](int t) -> uint32_t {
     uint64_t live;
     if (t < nlt) {
       if constexpr (ONE_BLOCK) {
@@ -543,10 +545,12 @@ void k_attn_fwd32d(FwdArgs a) {
       const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
       live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
     }
-    // this wave's 32 key rows; uniform, so the branches on it stay scalar
-    const uint32_t mine =
-        (uint32_t)__builtin_amdgcn_readfirstlane((int)(kh ? (uint32_t)(live >> 32) : (uint32_t)live));
-    if (mine == 0u) return;  // nothing live here, and m may still be -inf
+    // uniform, so the branches on it stay scalar
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(kh ? (uint32_t)(live >> 32) : (uint32_t)live));
+  };
+  // tile t with this wave's live rows `mine` (not zero)
+  auto compute = [&](auto sg, uint32_t mine, const RowsFrag32<DP>& vfr) {
+    const FwdStage32<DP>& S = stage(sg);
     f32x16 sc;
     score32_rows(S.k, f, sc, col, half, kh);
     if (mine != ~0u) {
@@ -594,10 +598,11 @@ void k_attn_fwd32d(FwdArgs a) {
     constexpr int SI = decltype(sg)::value;
     wait_vm<0>();
     barrier_copies();  // tile t is in stage SI; every wave is done with the other stage
+    const uint32_t mine = live_rows(t);  // zero: nothing live here, and m may still be -inf
     RowsFrag32<DP> vfr;
-    read_rows32(stage(sg).v, vfr, lane, half, kh);
+    if (mine) read_rows32(stage(sg).v, vfr, lane, half, kh);
     if (t + 1 < total) issue(Stage_<1 - SI>{}, t + 1);
-    compute(sg, t, vfr);
+    if (mine) compute(sg, mine, vfr);
   };
   if (total > 0) issue(Stage_<0>{}, 0);
   for (int t = 0; t < total; t += 2) {
