@@ -35,9 +35,9 @@ class Pack3DBlock(torch.nn.Module):
         self.fc1 = torch.nn.Linear(dim, mlp_ratio * dim, bias=False, **kw)
         self.fc2 = torch.nn.Linear(mlp_ratio * dim, dim, bias=False, **kw)
 
-    def load_oracle_params(self, params: dict):
-        """Copy a dict of weights in the layout of the fp64 reference block (names ln1_w, ln1_b,
-        qkv, proj, ln2_w, ln2_b, fc1, fc2)."""
+    def load_params(self, params: dict):
+        """Copy weights from a dict of tensors named ln1_w, ln1_b, qkv ([3C, C]), proj, ln2_w,
+        ln2_b, fc1 ([mlp_ratio C, C]) and fc2, each in torch.nn.Linear / LayerNorm layout."""
         with torch.no_grad():
             for mod, name in ((self.norm1.weight, "ln1_w"), (self.norm1.bias, "ln1_b"), (self.qkv.weight, "qkv"),
                               (self.proj.weight, "proj"), (self.norm2.weight, "ln2_w"), (self.norm2.bias, "ln2_b"),

@@ -84,7 +84,7 @@ def test_block_forward_backward_match_oracle(dtype):
     say(f"block {dtype}")
     w, coords, x, dy, params = _block_case(dtype)
     m = Pack3DBlock(w.heads * w.head_dim, w.heads, device=DEV, dtype=dtype)
-    m.load_oracle_params(params)
+    m.load_params(params)
     cd = coords.to(DEV)
     ix = p3.build_index(cd, w.block, w.radius)
     xd = x.to(DEV).requires_grad_()
@@ -136,7 +136,7 @@ def test_block_65k_forward_sampled():
     x = torch.from_numpy(gen.standard_normal((w.batch, w.tokens, c), dtype=np.float32)).to(dtype)
     params = {k: v.to(dtype).double() for k, v in ob.init_params(c, seed=95).items()}
     m = Pack3DBlock(c, w.heads, device=DEV, dtype=dtype)
-    m.load_oracle_params(params)
+    m.load_params(params)
     cd = coords.to(DEV)
     ix = p3.build_index(cd, w.block, w.radius)
     with torch.no_grad():
