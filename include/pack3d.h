@@ -211,7 +211,8 @@ size_t pack3d_workspace_bytes(const pack3d_index* index, const pack3d_attn* attn
  * are taken from them (relative to each volume's origin, which leaves every logit
  * unchanged).  Mismatched coordinates give unspecified values but no out-of-bounds
  * access.  Precision: fp32 inputs are computed in fp32 throughout; bf16 inputs use
- * bf16 matrix-core products with fp32 accumulation and fp32 softmax. */
+ * bf16 matrix-core products with fp32 accumulation and fp32 softmax.  q, k, v, out and
+ * the workspace must be 16-byte aligned (PACK3D_E_INVALID otherwise). */
 pack3d_status pack3d_forward(const pack3d_index* index, const pack3d_attn* attn,
                              const void* q_dev, const void* k_dev, const void* v_dev,
                              const int32_t* coords_dev, void* out_dev, float* lse_dev,
@@ -228,7 +229,8 @@ pack3d_status pack3d_forward(const pack3d_index* index, const pack3d_attn* attn,
  * pack3d_forward wrote for the same index, attn, q, k, v and coords (same workspace
  * pointer, untouched since), and the recomputation is skipped; results are then
  * bitwise equal to reuse_forward = 0.  A broken guarantee gives wrong gradients but
- * no out-of-bounds access.  Other values: PACK3D_E_INVALID. */
+ * no out-of-bounds access.  Other values: PACK3D_E_INVALID.  q, k, v, out, dout, dq, dk,
+ * dv and the workspace must be 16-byte aligned (PACK3D_E_INVALID otherwise). */
 pack3d_status pack3d_backward(const pack3d_index* index, const pack3d_attn* attn,
                               const void* q_dev, const void* k_dev, const void* v_dev,
                               const int32_t* coords_dev, const void* out_dev,

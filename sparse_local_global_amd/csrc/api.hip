@@ -112,8 +112,10 @@ pack3d_status run_backward(const pack3d_index* ix, const pack3d_attn* at, const 
   if (st != PACK3D_OK) return st;
   if (!q || !k || !v || !coords || !out || !lse || !dout || !dq || !dk || !dv || !ws)
     return set_error(PACK3D_E_INVALID, "%s: null pointer argument", who);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(ws))
-    return set_error(PACK3D_E_INVALID, "%s: q, k, v, out, dout and workspace must be 16-byte aligned", who);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(ws) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return set_error(PACK3D_E_INVALID, "%s: q, k, v, out, dout, dq, dk, dv and workspace must be 16-byte aligned",
+                     who);
   Dims d = make_dims(ix, at);
   d.in_stride = in_stride;
   d.grad_stride = grad_stride;

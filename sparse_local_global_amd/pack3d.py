@@ -274,6 +274,26 @@ def _check_act(name, t, shape, dtype):
         raise Pack3DError(E_INVALID, f"{name} must be a contiguous CUDA {dtype} tensor of shape {tuple(shape)}")
 
 
+# The library reads and writes these buffers at the sizes the index and the head count imply,
+# so every one a caller hands in is checked against them here.
+def _check_coords(index: Index, coords):
+    want = index.act_shape(1, 3)[:-2] + (3,)
+    if coords.dtype != torch.int32 or not coords.is_cuda or tuple(coords.shape) != tuple(want):
+        raise Pack3DError(E_INVALID, f"coords must be the index's CUDA int32 coordinates of shape {want}")
+
+
+def _check_lse(index: Index, lse, h):
+    want = (index.batch, h, index.tokens)
+    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != want or not lse.is_contiguous():
+        raise Pack3DError(E_INVALID, f"lse must be a contiguous CUDA float32 tensor of shape {want}")
+
+
+def _check_workspace(ws):
+    # its byte count is passed as the workspace size
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous():
+        raise Pack3DError(E_INVALID, "workspace must be a contiguous CUDA uint8 tensor")
+
+
 def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, with_summaries=True,
             workspace: torch.Tensor | None = None, out=None, lse=None, position_mode="axial"):
     """PACK3D forward.  q, k, v [B, N, H, D] (or [T, H, D] for a varlen index); returns (out
@@ -284,15 +304,19 @@ def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, wit
     attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries, position_mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_act(name, t, index.act_shape(h, d), q.dtype)
+    _check_coords(index, coords)
     need = workspace_bytes(index, attn)
     if need == 0:
         raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
     if out is None:
         out = torch.empty_like(q)
+    _check_act("out", out, index.act_shape(h, d), q.dtype)
     if lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    _check_lse(index, lse, h)
     _check(lib.pack3d_forward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(coords.contiguous()),
                               _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                               ctypes.c_void_p(_stream())))
@@ -312,8 +336,9 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
     attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries, position_mode)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check_act(name, t, index.act_shape(h, d), q.dtype)
-    if tuple(lse.shape) != (index.batch, h, index.tokens):
-        raise Pack3DError(E_INVALID, f"lse must be [{index.batch}, {h}, {index.tokens}]")
+    _check_coords(index, coords)
+    lse = lse.contiguous()
+    _check_lse(index, lse, h)
     need = workspace_bytes(index, attn, True)
     if need == 0:
         raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
@@ -321,9 +346,10 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
         if reuse_forward:
             raise Pack3DError(E_INVALID, "reuse_forward needs the forward's workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     _check(lib.pack3d_backward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v),
-                               _ptr(coords.contiguous()), _ptr(out), _ptr(lse.contiguous()), _ptr(dout.contiguous()),
+                               _ptr(coords.contiguous()), _ptr(out), _ptr(lse), _ptr(dout),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                                1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
     return dq, dk, dv
@@ -340,15 +366,19 @@ def forward_qkv(index: Index, qkv, coords, *, rope_base=10000.0, scale=None, wit
         raise Pack3DError(E_INVALID, f"qkv must be [{index.total}, 3, H, D]")
     attn = make_attn(qkv.dtype, h, d, rope_base, scale, with_summaries, position_mode)
     _check_act("qkv", qkv, (t, 3, h, d), qkv.dtype)
+    _check_coords(index, coords)
     need = workspace_bytes(index, attn)
     if need == 0:
         raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
+    _check_workspace(workspace)
     if out is None:
         out = torch.empty((t, h, d), dtype=qkv.dtype, device=qkv.device)
+    _check_act("out", out, (t, h, d), qkv.dtype)
     if lse is None:
         lse = torch.empty((index.batch, h, index.tokens), dtype=torch.float32, device=qkv.device)
+    _check_lse(index, lse, h)
     _check(lib.pack3d_forward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()),
                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                   ctypes.c_void_p(_stream())))
@@ -365,6 +395,9 @@ def backward_qkv(index: Index, qkv, coords, out, lse, dout, *, rope_base=10000.0
     _check_act("qkv", qkv, (index.total, 3, h, d), qkv.dtype)
     for name, x in (("out", out), ("dout", dout)):
         _check_act(name, x, (index.total, h, d), qkv.dtype)
+    _check_coords(index, coords)
+    lse = lse.contiguous()
+    _check_lse(index, lse, h)
     need = workspace_bytes(index, attn, True)
     if need == 0:
         raise Pack3DError(E_UNSUPPORTED, lib.pack3d_last_error().decode())
@@ -372,9 +405,10 @@ def backward_qkv(index: Index, qkv, coords, out, lse, dout, *, rope_base=10000.0
         if reuse_forward:
             raise Pack3DError(E_INVALID, "reuse_forward needs the forward's workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
+    _check_workspace(workspace)
     dqkv = torch.empty_like(qkv)
     _check(lib.pack3d_backward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()), _ptr(out),
-                                   _ptr(lse.contiguous()), _ptr(dout), _ptr(dqkv), _ptr(workspace),
+                                   _ptr(lse), _ptr(dout), _ptr(dqkv), _ptr(workspace),
                                    workspace.numel(), 1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
     return dqkv
 

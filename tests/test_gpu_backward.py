@@ -1,6 +1,8 @@
 """GPU backward (dq, dk, dv through the softmax, the block mean pooling and the RoPE)
 against the fp64 oracle.  Tolerances: max-abs 1e-5 (fp32 inputs), 2e-2 (bf16 inputs,
 fp32 accumulation)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -134,3 +136,35 @@ def test_backward_reusing_forward_workspace_bitwise(dtype):
         assert torch.equal(a, b)
     with pytest.raises(p3.Pack3DError):
         p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], reuse_forward=True)
+
+
+def test_backward_errors():
+    """Caller buffers of the wrong dtype or size, and gradient pointers that are not 16-byte
+    aligned, are refused before any launch."""
+    w = si.small_workload(grid=(4, 4, 8), block=(2, 2, 2), heads=1, head_dim=12, seed=1)
+    x = to_dev(si.make_inputs(w, torch.float32, with_grad=True))
+    ix = p3.build_index(x["coords"], w.block, 1)
+    out, lse = p3.forward(ix, x["q"], x["k"], x["v"], x["coords"])
+    attn = p3.make_attn(torch.float32, 1, 12)
+    ws = torch.empty(p3.workspace_bytes(ix, attn, True), dtype=torch.uint8, device=DEV)
+    args = (ix, x["q"], x["k"], x["v"], x["coords"], out)
+    for lse_bad in (lse.double(), lse[:, :, :-1]):
+        with pytest.raises(p3.Pack3DError) as e:
+            p3.backward(*args, lse_bad, x["do"])
+        assert e.value.status == p3.E_INVALID
+    with pytest.raises(p3.Pack3DError) as e:
+        p3.backward(*args, lse, x["do"], workspace=ws.view(torch.float32))
+    assert e.value.status == p3.E_INVALID
+    # C ABI with dq one element off 16-byte alignment (the buffer has room for that offset)
+    lib = p3.load_library()
+    g = torch.zeros(3 * w.tokens * 12 + 8, device=DEV)
+    base = g.data_ptr()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    dq = ctypes.c_void_p(base + 4)
+    dk = ctypes.c_void_p(base + 4 * (w.tokens * 12 + 4))
+    dv = ctypes.c_void_p(base + 4 * (2 * w.tokens * 12 + 8))
+    st = lib.pack3d_backward(ix.handle, ctypes.byref(attn), ptr(x["q"]), ptr(x["k"]), ptr(x["v"]), ptr(x["coords"]),
+                             ptr(out), ptr(lse), ptr(x["do"]), dq, dk, dv, ptr(ws), ws.numel(), 0, None)
+    torch.cuda.synchronize()
+    assert st == p3.E_INVALID and b"16-byte aligned" in lib.pack3d_last_error()
+    assert torch.count_nonzero(g) == 0

@@ -167,6 +167,19 @@ def test_forward_errors():
     with pytest.raises(p3.Pack3DError) as e:
         p3.forward(ix, x["q"].half(), x["k"].half(), x["v"].half(), x["coords"])
     assert e.value.status == p3.E_UNSUPPORTED
+    # buffers a caller hands in must have the sizes the index implies: refused before any launch
+    lse = torch.empty((1, 1, w.tokens), dtype=torch.float32, device=DEV)
+    for kw in (dict(out=torch.empty_like(x["q"])[:, :-1]),
+               dict(out=torch.empty_like(x["q"]).transpose(2, 3)),
+               dict(lse=lse.double()),
+               dict(lse=lse[:, :, :-1]),
+               dict(workspace=ws.view(torch.float32))):
+        with pytest.raises(p3.Pack3DError) as e:
+            p3.forward(ix, x["q"], x["k"], x["v"], x["coords"], **kw)
+        assert e.value.status == p3.E_INVALID, kw
+    with pytest.raises(p3.Pack3DError) as e:
+        p3.forward(ix, x["q"], x["k"], x["v"], x["coords"][:, :-1].contiguous())
+    assert e.value.status == p3.E_INVALID
 
 
 @pytest.mark.parametrize("scale", [3.0, 6.0])
