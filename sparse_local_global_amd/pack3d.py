@@ -478,19 +478,23 @@ class Pack3DAttention(torch.autograd.Function):
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
         out, lse = forward(index, q, k, v, coords, rope_base=rope_base, scale=scale,
                            with_summaries=with_summaries, workspace=ws, position_mode=position_mode)
-        ctx.save_for_backward(q, k, v, out, lse)
-        ctx.index, ctx.coords, ctx.workspace = index, coords, ws
+        # coords go through autograd's saved tensors too, so changing them in place before
+        # the backward is an error rather than gradients for other coordinates
+        ctx.save_for_backward(q, k, v, out, lse, coords)
+        ctx.index, ctx.workspace = index, ws
         ctx.opts = (rope_base, scale, with_summaries, position_mode)
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, out, lse = ctx.saved_tensors
+        q, k, v, out, lse, coords = ctx.saved_tensors
         rope_base, scale, with_summaries, position_mode = ctx.opts
-        dq, dk, dv = backward(ctx.index, q, k, v, ctx.coords, out, lse, dout.contiguous(), rope_base=rope_base,
-                              scale=scale, with_summaries=with_summaries, workspace=ctx.workspace,
-                              reuse_forward=True, position_mode=position_mode)
-        ctx.workspace = None
+        # the first backward reuses the forward's intermediates and frees them; a second
+        # one (retain_graph) recomputes them
+        ws, ctx.workspace = ctx.workspace, None
+        dq, dk, dv = backward(ctx.index, q, k, v, coords, out, lse, dout.contiguous(), rope_base=rope_base,
+                              scale=scale, with_summaries=with_summaries, workspace=ws,
+                              reuse_forward=ws is not None, position_mode=position_mode)
         return dq, dk, dv, None, None, None, None, None, None
 
 
@@ -514,19 +518,19 @@ class Pack3DAttentionQKV(torch.autograd.Function):
         ws = torch.empty(need, dtype=torch.uint8, device=qkv.device)
         out, lse = forward_qkv(index, qkv, coords, rope_base=rope_base, scale=scale, with_summaries=with_summaries,
                                workspace=ws, position_mode=position_mode)
-        ctx.save_for_backward(qkv, out, lse)
-        ctx.index, ctx.coords, ctx.workspace = index, coords, ws
+        ctx.save_for_backward(qkv, out, lse, coords)
+        ctx.index, ctx.workspace = index, ws
         ctx.opts = (rope_base, scale, with_summaries, position_mode)
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        qkv, out, lse = ctx.saved_tensors
+        qkv, out, lse, coords = ctx.saved_tensors
         rope_base, scale, with_summaries, position_mode = ctx.opts
-        dqkv = backward_qkv(ctx.index, qkv, ctx.coords, out, lse, dout.contiguous(), rope_base=rope_base, scale=scale,
-                            with_summaries=with_summaries, workspace=ctx.workspace, reuse_forward=True,
+        ws, ctx.workspace = ctx.workspace, None
+        dqkv = backward_qkv(ctx.index, qkv, coords, out, lse, dout.contiguous(), rope_base=rope_base, scale=scale,
+                            with_summaries=with_summaries, workspace=ws, reuse_forward=ws is not None,
                             position_mode=position_mode)
-        ctx.workspace = None
         return dqkv, None, None, None, None, None, None
 
 

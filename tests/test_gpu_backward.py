@@ -96,11 +96,23 @@ def test_autograd_wrapper():
     xd = to_dev(x)
     ix = p3.build_index(xd["coords"], w.block, w.radius)
     q, k, v = (xd[n].clone().requires_grad_() for n in ("q", "k", "v"))
-    o = p3.attention(q, k, v, ix, xd["coords"])
-    (o * xd["do"]).sum().backward()
+    coords = xd["coords"].clone()
+    o = p3.attention(q, k, v, ix, coords)
+    (o * xd["do"]).sum().backward(retain_graph=True)
     ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius)
     for g, rr in zip((q.grad, k.grad, v.grad), ref):
         assert max_err(g, rr) < TOL[dtype]
+    # a second backward through the retained graph recomputes the freed intermediates:
+    # the gradients accumulate to exactly twice the first ones
+    first = [t.grad.clone() for t in (q, k, v)]
+    (o * xd["do"]).sum().backward()
+    for t, g in zip((q, k, v), first):
+        assert torch.equal(t.grad, 2 * g)
+    # coordinates changed in place after the forward are caught by autograd
+    o = p3.attention(q, k, v, ix, coords)
+    coords.add_(1)
+    with pytest.raises(RuntimeError, match="modified by an inplace operation"):
+        (o * xd["do"]).sum().backward()
 
 
 def test_backward_poisoned_workspace():
