@@ -135,6 +135,11 @@ class Index:
         self.total = batch * tokens if offsets is None else self.offsets[-1]
         self.ragged = ragged
 
+    @property
+    def device(self) -> torch.device:
+        """The GPU holding the index's tables; every tensor used with the index must be on it."""
+        return self.tables_buffer.device
+
     def act_shape(self, h, d):
         """Shape of q, k, v, out and the gradients for this layout."""
         return (self.batch, self.tokens, h, d) if self.offsets is None else (self.total, h, d)
@@ -209,8 +214,9 @@ def measure_blocks(coords: torch.Tensor, block_shape, *, offsets=None) -> int:
     bs = (ctypes.c_int32 * 3)(*block_shape)
     scratch = torch.empty(64 * b, dtype=torch.uint8, device=coords.device)
     out = ctypes.c_int32()
-    _check(lib.pack3d_measure_blocks(_ptr(coords.contiguous()), ctypes.byref(p), bs, _ptr(scratch), scratch.numel(),
-                                     ctypes.c_void_p(_stream()), ctypes.byref(out)))
+    with torch.cuda.device(coords.device):
+        _check(lib.pack3d_measure_blocks(_ptr(coords.contiguous()), ctypes.byref(p), bs, _ptr(scratch),
+                                         scratch.numel(), ctypes.c_void_p(_stream()), ctypes.byref(out)))
     return out.value
 
 
@@ -244,8 +250,9 @@ def build_index(coords: torch.Tensor, block_shape, local_radius: int, order_hint
         raise Pack3DError(E_INVALID, "invalid batch layout, block shape or radius")
     tables = torch.empty(nbytes, dtype=torch.uint8, device=coords.device)
     handle = ctypes.c_void_p()
-    _check(lib.pack3d_build_index(_ptr(coords), ctypes.byref(p), bs, local_radius, _ptr(tables),
-                                  nbytes, ctypes.c_void_p(_stream()), ctypes.byref(handle)))
+    with torch.cuda.device(coords.device):
+        _check(lib.pack3d_build_index(_ptr(coords), ctypes.byref(p), bs, local_radius, _ptr(tables),
+                                      nbytes, ctypes.c_void_p(_stream()), ctypes.byref(handle)))
     nmax = n if offsets is None else max(int(offsets[i + 1]) - int(offsets[i]) for i in range(b))
     return Index(handle, tables, b, nmax, block_shape, local_radius, offsets, ragged)
 
@@ -288,6 +295,12 @@ def _check_lse(index: Index, lse, h):
         raise Pack3DError(E_INVALID, f"lse must be a contiguous CUDA float32 tensor of shape {want}")
 
 
+def _check_device(index: Index, *tensors):
+    for t in tensors:
+        if t is not None and t.device != index.device:
+            raise Pack3DError(E_INVALID, f"tensors must be on the index's device {index.device}, not {t.device}")
+
+
 def _check_workspace(ws):
     # its byte count is passed as the workspace size
     if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous():
@@ -317,9 +330,11 @@ def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, wit
     if lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     _check_lse(index, lse, h)
-    _check(lib.pack3d_forward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(coords.contiguous()),
-                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-                              ctypes.c_void_p(_stream())))
+    _check_device(index, q, k, v, coords, workspace, out, lse)
+    with torch.cuda.device(index.device):
+        _check(lib.pack3d_forward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(coords.contiguous()),
+                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                  ctypes.c_void_p(_stream())))
     return out, lse
 
 
@@ -348,10 +363,12 @@ def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check_workspace(workspace)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    _check(lib.pack3d_backward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v),
-                               _ptr(coords.contiguous()), _ptr(out), _ptr(lse), _ptr(dout),
-                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                               1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
+    _check_device(index, q, k, v, coords, out, lse, dout, workspace)
+    with torch.cuda.device(index.device):
+        _check(lib.pack3d_backward(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(coords.contiguous()), _ptr(out), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                   1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
     return dq, dk, dv
 
 
@@ -379,9 +396,11 @@ def forward_qkv(index: Index, qkv, coords, *, rope_base=10000.0, scale=None, wit
     if lse is None:
         lse = torch.empty((index.batch, h, index.tokens), dtype=torch.float32, device=qkv.device)
     _check_lse(index, lse, h)
-    _check(lib.pack3d_forward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()),
-                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-                                  ctypes.c_void_p(_stream())))
+    _check_device(index, qkv, coords, workspace, out, lse)
+    with torch.cuda.device(index.device):
+        _check(lib.pack3d_forward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()),
+                                      _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                      ctypes.c_void_p(_stream())))
     return out, lse
 
 
@@ -407,9 +426,11 @@ def backward_qkv(index: Index, qkv, coords, out, lse, dout, *, rope_base=10000.0
         workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
     _check_workspace(workspace)
     dqkv = torch.empty_like(qkv)
-    _check(lib.pack3d_backward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()), _ptr(out),
-                                   _ptr(lse), _ptr(dout), _ptr(dqkv), _ptr(workspace),
-                                   workspace.numel(), 1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
+    _check_device(index, qkv, coords, out, lse, dout, workspace)
+    with torch.cuda.device(index.device):
+        _check(lib.pack3d_backward_qkv(index.handle, ctypes.byref(attn), _ptr(qkv), _ptr(coords.contiguous()), _ptr(out),
+                                       _ptr(lse), _ptr(dout), _ptr(dqkv), _ptr(workspace),
+                                       workspace.numel(), 1 if reuse_forward else 0, ctypes.c_void_p(_stream())))
     return dqkv
 
 
