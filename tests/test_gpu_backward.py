@@ -10,7 +10,8 @@ import torch
 import oracle
 import synthetic_inputs as si
 import sparse_local_global_amd.pack3d as p3
-from tests.gpu_cases import DEV, TOL, max_err, say, to_dev
+from tests.dense_ref import torch_axial_rope
+from tests.gpu_cases import DEV, TOL, max_err, sample_blocks, say, to_dev
 from tests.test_gpu_forward import CASES
 
 pytestmark = pytest.mark.gpu
@@ -65,6 +66,47 @@ def test_backward_65k_training_workload_one_head():
         gg = g[vol][:, head].float().cpu().double().numpy()
         assert np.abs(gg - rr[vol][:, head]).max() < TOL[dtype], name
         assert torch.isfinite(g).all(), name
+
+
+def test_backward_524k_sampled_dq_and_identities():
+    """The 524k workload: one volume of 32x128x128 tokens in 256-token blocks (4x8x8), so each
+    block is four 64-query tiles and a query sees up to 6,912 local keys and 2,025 summaries.
+    dq of sampled query blocks against the oracle.  dk and dv need every query, so over all
+    524,288 tokens they are held to two exact identities of the method (each query's weights
+    over keys and summaries sum to one, and a block mean hands a summary's gradient to its
+    members in full):
+        sum_j dv_j = sum_i dO_i        and        sum_j R_j dk_j = 0
+    per (head, channel), R_j the token's rotation.  Bound: 2^-7 of sum_i |dO_i| (bf16 products
+    and bf16 gradients, as at the block-count limit)."""
+    w = si.WORKLOADS["524k"]
+    dtype = torch.bfloat16
+    say("backward 524k")
+    x = si.make_inputs(w, dtype, with_grad=True)
+    x["do"] = (x["do"].float() + 0.75).to(dtype)   # a mean offset makes the dv identity sensitive
+    xd = to_dev(x)
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    out, lse = p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], rope_base=w.rope_base)
+    dq, dk, dv = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"],
+                             rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g).all()
+    nb = tuple(g // b for g, b in zip(w.grid, w.block))
+    blocks = sample_blocks(nb, count=6, seed=w.seed)
+    dq_ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius,
+                             query_blocks=blocks)[0]
+    mask = ~np.isnan(dq_ref)
+    assert mask.sum() == len(blocks) * int(np.prod(w.block)) * w.heads * w.head_dim
+    assert max_err(dq, dq_ref, mask) < TOL[dtype]
+    del dq_ref, mask
+    do64 = xd["do"][0].double()
+    scale = do64.abs().sum(0)                                            # [H, D]
+    gap = dv[0].double().sum(0) - do64.sum(0)
+    assert (gap.abs() <= 2.0 ** -7 * scale).all(), float((gap.abs() / scale).max())
+    c = x["coords"][0].long()
+    rot = torch_axial_rope(dk[0].double().cpu(), c - c.min(0).values, w.rope_base).sum(0)
+    scale = scale.cpu()
+    assert (rot.abs() <= 2.0 ** -7 * scale).all(), float((rot.abs() / scale).max())
 
 
 def test_backward_deterministic_and_repacking_bitwise():
