@@ -13,9 +13,11 @@ workspace (as the autograd wrapper does).  Inputs are resident in HBM before the
 timed region starts.
 
 Printed: one JSON line with the contract fields, the roofline of the dominant
-kernel (fused attention forward) from HIP events recorded by the library around
-each launch on its stream, the windowed-only (local keys only) latency of the same
-kernel, and the fp64 CPU oracle timed on a bounded sample (rank 0, one GPU).
+kernel (the matrix-core kernel with the most time per step: bwd_dq in the training
+step, the fused attention forward in a forward-only run) from HIP events recorded by
+the library around each launch on its stream, every kernel's rate, the windowed-only
+(local keys only) latency of the attention forward, and the fp64 CPU oracle timed on
+a bounded sample (rank 0, one GPU).
 """
 from __future__ import annotations
 
@@ -340,6 +342,9 @@ def main(argv=None) -> int:
         "rope_pool_bwd": (6.0 * act, "hbm"),                # recomputation (backward without reuse)
         "bwd_pre": (3.0 * act, "hbm"),                      # read dO, O; write dO canonical
     }
+    # matrix-core work the kernel executes where it exceeds the algorithmic count (reported
+    # beside it, never as the numerator): bwd_dq recomputes S and dP for its dQ product
+    executed = {"bwd_dq": 6.0 * d * (local + summ) * bh}
     kern = {}
     for name, (n, t) in prof.items():
         avg = t / max(n, 1)
@@ -350,6 +355,10 @@ def main(argv=None) -> int:
             if bound == "mfma":
                 entry.update(bound="mfma", flop_per_launch=amount, tflops=rate / 1e12,
                              frac=rate / 1e12 / PEAK_BF16_TFLOPS)
+                if name in executed:
+                    erate = executed[name] / (avg * 1e-3) / 1e12
+                    entry.update(executed_flop_per_launch=executed[name], executed_tflops=erate,
+                                 executed_frac=erate / PEAK_BF16_TFLOPS)
             else:
                 entry.update(bound="hbm", bytes_per_launch=amount, gbs=rate / 1e9, frac=rate / 1e9 / PEAK_HBM_GBS)
         kern[name] = entry
@@ -380,7 +389,8 @@ def main(argv=None) -> int:
                    "accumulation": "fp32"},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": dk["frac"], "traffic": stored_traffic(dominant),
-                     "flop_per_launch": dk["flop_per_launch"], "avg_launch_ms": dk["avg_ms"]},
+                     "flop_per_launch": dk["flop_per_launch"], "avg_launch_ms": dk["avg_ms"],
+                     **({"executed_frac": dk["executed_frac"]} if "executed_frac" in dk else {})},
         "kernels": kern,
         "forward_ms": ms_fwd,
         "forward_tokens_per_s": tokens / (ms_fwd * 1e-3),
