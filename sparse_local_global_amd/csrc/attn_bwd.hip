@@ -758,10 +758,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     else if constexpr (decltype(st)::value == 1) return s1;
     else return s2;
   };
+  // Tiles are issued, and computed, in increasing order, so cursors replace the divisions
+  // (scalar code, but issued by this wave) that would find each tile's query block and
+  // its block-grid coordinates.
+  int iss_q = q_begin, iss_s = 0;  // next tile to issue: query block, sub-tile
+  int cmp_s = 0;                   // sub-tile of the next tile to compute
+  int qz = q_begin / (nby * nbx), qy = (q_begin / nbx) % nby, qx = q_begin % nbx;  // its block
   auto issue = [&](auto st, int t) {
     LocStage32<DP>& S = stage(st);
-    const int qb = q_begin + t / tpb, qs = t - (t / tpb) * tpb;
-    const int row0 = qb * bvol + qs * kTile;
+    const int row0 = iss_q * bvol + iss_s * kTile;
+    if (++iss_s == tpb) {
+      iss_s = 0;
+      ++iss_q;
+    }
     const int w = wave_id(), r = 16 * w + (lane & 15);
     // (issue_at in this generic lambda costs another kernel's host-side stub, see
     // bwd_local32; the row form serves both layouts)
@@ -773,10 +782,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   auto compute = [&](auto st, int t) {
     const LocStage32<DP>& S = stage(st);
-    const int qb = q_begin + t / tpb;
-    const int qz = qb / (nby * nbx), qy = (qb / nbx) % nby, qx = qb % nbx;
     const int cheb = max(max(abs(qz - sz), abs(qy - sy)), abs(qx - sx));
     const bool masked = sid >= a.nblk || cheb <= a.radius;  // per lane: this summary column
+    if (++cmp_s == tpb) {  // the next tile starts the next query block (raster order)
+      cmp_s = 0;
+      if (++qx == nbx) {
+        qx = 0;
+        if (++qy == nby) {
+          qy = 0;
+          ++qz;
+        }
+      }
+    }
     // dp = <dO, Vbar> - delta: the products accumulate onto -delta; slots 4j .. 4j+3 are
     // rows 32qh + 8j + 4half + e
     f32x16 s, dp, nd;
