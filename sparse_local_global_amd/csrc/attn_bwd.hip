@@ -591,18 +591,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     else if constexpr (decltype(st)::value == 1) return s1;
     else return s2;
   };
+  // ONE_BLOCK: tiles are issued in order, so a cursor (entry of the neighbour list, 64-row
+  // tile within that block) replaces a division per tile
+  const int tpb = a.tiles_per_block;
+  int cur_entry = 0, cur_sub = 0;
   auto issue = [&](auto st, int t) {
     LocStage32<DP>& S = stage(st);
     const int j0 = t * kTile;
-    const VirtualRows vr(sm.list, bvol, j0);
     const int w = wave_id(), r = 16 * w + (lane & 15);
     if constexpr (ONE_BLOCK) {
-      const int row0 = vr.blk0 * bvol + vr.off0;
+      const int row0 = __builtin_amdgcn_readfirstlane(sm.list[cur_entry]) * bvol + cur_sub * kTile;
+      if (++cur_sub == tpb) {
+        cur_sub = 0;
+        ++cur_entry;
+      }
       dma.issue_at(qrot, S.q, (uint32_t)row0 * DP);
       dma.issue_at(doc, S.g, (uint32_t)row0 * DP);
       issue_rows16(lsec, &S.lse2[16 * w], (uint32_t)(row0 + r) * 4u);
       issue_rows16(dlt, &S.ndelta[16 * w], (uint32_t)(row0 + r) * 4u);
     } else {
+      const VirtualRows vr(sm.list, bvol, j0);
       const int valid = nq - j0 < kTile ? nq - j0 : kTile;
       dma.issue(qrot, S.q, valid, [&](int rr) { return vr.row(rr) * DP; });
       dma.issue(doc, S.g, valid, [&](int rr) { return vr.row(rr) * DP; });
@@ -1023,16 +1031,24 @@ void k_bwd_dq(BwdArgs a) {
   struct Stage {
     RowRegs<T, DP> k, v;
   } st0, st1;
+  // ONE_BLOCK: local tiles are fetched in order, so a cursor (entry of the neighbour list,
+  // 64-row tile within that block) replaces a division per tile
+  const int tpb = a.tiles_per_block;
+  int cur_entry = 0, cur_sub = 0;
   auto fetch = [&](Stage& S, int t) {
     if (t < nlt) {
       const int j0 = t * kTile;
       const int valid = nkeys - j0 < kTile ? nkeys - j0 : kTile;
-      const VirtualRows vr(sm.list, bvol, j0);
       if constexpr (ONE_BLOCK) {
-        const int row0 = vr.blk0 * bvol + vr.off0;
+        const int row0 = __builtin_amdgcn_readfirstlane(sm.list[cur_entry]) * bvol + cur_sub * kTile;
+        if (++cur_sub == tpb) {
+          cur_sub = 0;
+          ++cur_entry;
+        }
         S.k.fetch_at(krot, (uint32_t)row0 * DP);
         S.v.fetch_at(vrow, (uint32_t)row0 * DP);
       } else {
+        const VirtualRows vr(sm.list, bvol, j0);
         S.k.fetch(krot, valid, [&](int r) { return vr.row(r) * DP; });
         S.v.fetch(vrow, valid, [&](int r) { return vr.row(r) * DP; });
       }
