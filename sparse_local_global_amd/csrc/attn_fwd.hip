@@ -415,9 +415,14 @@ struct FwdStage32 {
   RowTile<bf16, DP> k, v;
 };
 
+// Local key tiles whose live-row masks k_attn_fwd32d reads into LDS before its loop when
+// slots can be empty (small enough to keep three workgroups per CU).
+constexpr int kFwdLiveTiles = 32;
+
 struct FwdSmem32d {
   int list[kMaxSlots];
   uint32_t mask[kMaxBlocks / 32];
+  uint64_t live[kFwdLiveTiles];  // local tile t: bit r = key row r holds a token (empty slots only)
   int nloc;
 };
 
@@ -529,15 +534,30 @@ void k_attn_fwd32d(FwdArgs a) {
   // This wave's live key rows of tile t (bit r: row 32kh + r).  It runs before the next
   // tile's copies are issued: with empty slots it loads occupancy words, and a wait for
   // those would otherwise also wait for the copies.
+  // With empty slots the local tiles' occupancy comes from global memory.  Up to
+  // kFwdLiveTiles tiles it is read here, before the loop, one tile per wave at a time: in
+  // the loop each such load would hold up its step for a whole memory latency.  The first
+  // step's barrier orders these LDS writes before their reads.
+  const bool live_table = a.holes && nlt <= kFwdLiveTiles;
+  if (live_table) {
+    for (int t = wave; t < nlt; t += kThreads / 64) {
+      const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
+      const uint64_t lv = occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+      if (lane == 0) sm.live[t] = lv;
+    }
+  }
+  auto tile_occupancy = [&](int t, int valid) -> uint64_t {
+    return live_table ? sm.live[t] : occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+  };
   auto live_rows = [&](int t) -> uint32_t {
     uint64_t live;
     if (t < nlt) {
       if constexpr (ONE_BLOCK) {
-        live = a.holes ? occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), kTile) : ~0ull;
+        live = a.holes ? tile_occupancy(t, kTile) : ~0ull;
       } else {
         const int valid = nkeys - t * kTile < kTile ? nkeys - t * kTile : kTile;
         live = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
-        if (a.holes) live &= occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), valid);
+        if (a.holes) live &= tile_occupancy(t, valid);
       }
     } else {
       const int ts = t - nlt, r0 = ts * kTile;
