@@ -52,6 +52,7 @@ struct RopeArgs {
   const float2* tab;
   void* qrot; void* krot; void* vr; void* kbar; void* vbar;
   int NC, H, D, Dp, nblk, nblkp, bvol, heads_per_group, holes;
+  int pool;  // 0: windowed-only attention reads no block means, so none are formed
   int64_t in_stride;  // elements between consecutive tokens of q, k, v
   int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
 };
@@ -65,8 +66,9 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   const int NC = a.NC, H = a.H, D = a.D, Dp = a.Dp, bvol = a.bvol;
   const int gw = D / GROUPS, half = gw / 2;
   constexpr int groups = GROUPS;
-  const int ntok = bvol < kChunk ? bvol : kChunk;
-  const int nchunk = bvol / ntok;
+  const int ntok = bvol < kChunk ? bvol : kChunk;  // rows of the staging tiles
+  const int nchunk = (bvol + kChunk - 1) / kChunk;   // the last chunk may be partial (|b| = 40, 48, 56)
+  const bool pool = a.pool != 0;
   // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1], vl[ntok][Dp+1] (float)
   int* s_src = (int*)smem;
   int* s_rel = s_src + bvol;
@@ -96,8 +98,6 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   T* krot = (T*)a.krot;
   T* vr = (T*)a.vr;
   const int pchunks = half / VEC;         // VEC-wide pieces per half group
-  const int rope_items = ntok * groups * pchunks;
-  const int v_items = ntok * (D / VEC);
   const int h0 = hg * a.heads_per_group;
 
   for (int hh = 0; hh < a.heads_per_group; ++hh) {
@@ -105,7 +105,10 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
     const int64_t bh = (int64_t)b * H + h;
     float csum = 0.f;   // K~ column tid (tid < Dp) or V column tid - Dp (tid < 2 Dp)
     for (int ch = 0; ch < nchunk; ++ch) {
-      const int t0 = ch * ntok;
+      const int t0 = ch * kChunk;
+      const int cnt = bvol - t0 < kChunk ? bvol - t0 : kChunk;  // tokens of this chunk
+      const int rope_items = cnt * groups * pchunks;
+      const int v_items = cnt * (D / VEC);
       // rotate q and k
       for (int it = tid; it < rope_items; it += 256) {
         const int tok = it / (groups * pchunks);
@@ -139,8 +142,10 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           const float ky2 = ROTATE ? y1 * r.y + y2 * r.x : y2;
           ok1.v[e] = from_f<T>(ky1);
           ok2.v[e] = from_f<T>(ky2);
-          kl[tok * ls + col1 + e] = ky1;
-          kl[tok * ls + col2 + e] = ky2;
+          if (pool) {
+            kl[tok * ls + col1 + e] = ky1;
+            kl[tok * ls + col2 + e] = ky2;
+          }
         }
         const int64_t out_row = (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp;
         *(Vec<T, VEC>*)(qrot + out_row + col1) = oq1;
@@ -161,33 +166,38 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           for (int e = 0; e < VEC; ++e) x.v[e] = from_f<T>(0.f);
         }
         *(Vec<T, VEC>*)(vr + (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp + col) = x;
+        if (pool) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) vl[tok * ls + col + e] = to_f(x.v[e]);
+          for (int e = 0; e < VEC; ++e) vl[tok * ls + col + e] = to_f(x.v[e]);
+        }
       }
       // zero padding columns D..Dp of the rows and of the staged tiles
       if (Dp > D) {
         const int pad = Dp - D;
-        for (int it = tid; it < ntok * pad; it += 256) {
+        for (int it = tid; it < cnt * pad; it += 256) {
           const int tok = it / pad, col = D + it - tok * pad;
           const int64_t out_row = (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp;
           qrot[out_row + col] = from_f<T>(0.f);
           krot[out_row + col] = from_f<T>(0.f);
           vr[out_row + col] = from_f<T>(0.f);
-          kl[tok * ls + col] = 0.f;
-          vl[tok * ls + col] = 0.f;
+          if (pool) {
+            kl[tok * ls + col] = 0.f;
+            vl[tok * ls + col] = 0.f;
+          }
         }
       }
+      if (!pool) continue;  // no LDS staging to read back: the next chunk needs no barrier
       __syncthreads();
       // column sums over the chunk: threads 0 .. Dp-1 sum K~ columns, Dp .. 2Dp-1 V columns
       if (tid < 2 * Dp) {
         const float* col = tid < Dp ? kl + tid : vl + (tid - Dp);
         float cs = 0.f;
-        for (int t = 0; t < ntok; ++t) cs += col[t * ls];
+        for (int t = 0; t < cnt; ++t) cs += col[t * ls];
         csum += cs;
       }
       __syncthreads();
     }
-    if (tid < 2 * Dp) {
+    if (pool && tid < 2 * Dp) {
       // mean over the tokens present (|b| on a full grid); an empty block's sums are 0
       const int cnt = a.holes ? a.count[(int64_t)b * a.nblk + blk] : bvol;
       const float inv = cnt > 0 ? 1.0f / (float)cnt : 0.f;
@@ -245,6 +255,7 @@ pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack
   a.tab = (const float2*)(ws + w.rope);
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
   a.in_stride = d.in_stride;
+  a.pool = at->with_summaries ? 1 : 0;
   a.NC = d.NC; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.pos_mode = d.pos_mode; a.groups = d.groups; a.gw = d.gw; a.half = d.half; a.trows = d.trows;
   // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all

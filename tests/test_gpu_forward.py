@@ -21,9 +21,19 @@ def _canonical(x, ix_ref, v):
     return x[v][ix_ref[v]["perm"]]
 
 
-@pytest.mark.parametrize("name,dtype", [("tiny", torch.float32), ("16k", torch.bfloat16)])
+# 48-token blocks: the RoPE / pooling pass stages tokens 32 at a time, so each block ends
+# in a partial chunk whose tokens must be gathered, rotated and pooled like the others
+INTERMEDIATE_CASES = {
+    "tiny": si.WORKLOADS["tiny"],
+    "16k": si.WORKLOADS["16k"],
+    "bvol48": si.small_workload(grid=(8, 8, 12), block=(4, 4, 3), heads=2, head_dim=96, packing="random", seed=23),
+}
+
+
+@pytest.mark.parametrize("name,dtype", [("tiny", torch.float32), ("16k", torch.bfloat16),
+                                        ("bvol48", torch.float32), ("bvol48", torch.bfloat16)])
 def test_intermediates_rope_and_pooling(name, dtype):
-    w = si.WORKLOADS[name]
+    w = INTERMEDIATE_CASES[name]
     say(f"intermediates {name} {dtype}")
     x, ix, out, lse, ws = gpu_forward(w, dtype)
     views = p3.workspace_views(ix, (w.batch, w.tokens, w.heads, w.head_dim), dtype, ws, w.rope_base)
@@ -66,6 +76,12 @@ CASES = [
     ((8, 8, 8), (4, 4, 4), 0, 1, 66, "random", 1, torch.float32),    # r = 0, Dp 96 with padding
     ((4, 8, 8), (2, 2, 2), 3, 2, 24, "raster", 1, torch.bfloat16),   # r = 3 (slots 343)
     ((8, 8, 8), (2, 2, 4), 1, 2, 90, "morton", 1, torch.bfloat16),   # Dp 96 with padding, bvol 16
+    # blocks of 40, 48 and 56 tokens: the RoPE / pooling pass stages 32 tokens at a time,
+    # so the last chunk of each block is partial
+    ((8, 8, 12), (4, 4, 3), 1, 2, 96, "random", 1, torch.float32),   # bvol 48
+    ((8, 8, 12), (4, 4, 3), 1, 2, 96, "random", 1, torch.bfloat16),  # bvol 48
+    ((4, 8, 10), (2, 4, 5), 1, 2, 48, "morton", 1, torch.bfloat16),  # bvol 40, Dp 64
+    ((4, 8, 14), (2, 4, 7), 1, 2, 96, "block", 1, torch.float32),    # bvol 56
 ]
 
 
