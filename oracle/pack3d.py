@@ -308,69 +308,6 @@ def _key_rows(local, bvol, present=None):
     return rows if present is None else rows[present[rows]]
 
 
-# --------------------------------------------------------------------------
-# Forward
-# --------------------------------------------------------------------------
-
-def _f64(t) -> np.ndarray:
-    """Exact conversion of a numpy array or a CPU torch tensor to fp64 numpy."""
-    if hasattr(t, "detach"):
-        t = t.detach().to("cpu")
-        import torch  # local: the oracle itself does not need torch
-        return t.to(torch.float64).numpy()
-    return np.asarray(t, dtype=np.float64)
-
-
-def _canonical(x, perm, present):
-    """Rows of x [N, ...] in canonical order; empty slots hold zeros."""
-    out = np.zeros((perm.shape[0], *x.shape[1:]), dtype=np.float64)
-    out[present] = x[perm[present]]
-    return out
-
-
-def _prepare(q, k, v, coords, block_shape, r, base, rope_coords=None, position_mode="axial", ragged=False,
-             offsets=None):
-    q, k, v = _f64(q), _f64(k), _f64(v)
-    coords = np.asarray(coords.numpy() if hasattr(coords, "numpy") else coords)
-    if coords.ndim == 2 and offsets is None:
-        coords = coords[None]
-    index = build_index(coords, block_shape, r, ragged=ragged, offsets=offsets)
-    rc = coords if rope_coords is None else np.asarray(rope_coords)
-    qs, ks, vs, rcs = (split_volumes(x, offsets) for x in (q, k, v, rc))
-    vols = []
-    for vi, ix in enumerate(index):
-        perm, present = ix["perm"], ix["present"]       # canonical slot -> packed position (-1: empty)
-        pos = np.arange(ix["n"])
-        qt = _canonical(rotate(qs[vi], rcs[vi], pos, base, position_mode), perm, present)
-        kt = _canonical(rotate(ks[vi], rcs[vi], pos, base, position_mode), perm, present)
-        vc = _canonical(vs[vi], perm, present)
-        cnt = ix["count"] if ragged else None
-        vols.append(dict(ix=ix, qt=qt, kt=kt, vc=vc,
-                         kbar=pool_blocks(kt, ix["bvol"], cnt), vbar=pool_blocks(vc, ix["bvol"], cnt)))
-    return q, k, v, coords, vols
-
-
-def _local_blocks(ix, qb):
-    return [int(n) for n in ix["nbr"][qb] if n >= 0]
-
-
-def _summary_blocks(ix, qb, local):
-    """Occupied blocks outside the local neighbourhood, in block-id order."""
-    mask = ix["count"] > 0
-    mask[local] = False
-    return np.nonzero(mask)[0]
-
-
-def _key_rows(local, bvol, present=None):
-    rows = np.concatenate([np.arange(n * bvol, (n + 1) * bvol) for n in local])
-    return rows if present is None else rows[present[rows]]
-
-
-def _out_like(q, offsets, bsz, nmax, h):
-    """fp64 NaN outputs: o shaped like q, lse [B, H, max N_v]."""
-    return np.full(q.shape, np.nan), np.full((bsz, h, nmax), np.nan)
-
-
 def _join(parts, offsets):
     """Per-volume arrays back to the caller's layout: stacked [B, N, ...] or flat [T, ...]."""
     return np.stack(parts) if offsets is None else np.concatenate(parts)

@@ -6,7 +6,6 @@ one softmax over a masked [keys | summaries] logit row).  Source of the
 operator: "Geometry Matters in Packed 3D Attention", abstract ("trainable at
 scale"); gradients are taken with respect to the unrotated q, k, v.
 """
-import math
 
 import numpy as np
 import pytest
@@ -14,6 +13,7 @@ import torch
 
 import oracle
 import synthetic_inputs as si
+from tests.dense_ref import dense_masked
 
 
 def _rope_torch(x, c, base):
@@ -31,28 +31,9 @@ def _rope_torch(x, c, base):
 
 
 def _dense_masked(q, k, v, c, block, r, base, with_summaries=True):
-    """q, k, v [N, H, D] fp64 tensors; returns o [N, H, D]."""
-    n, h, d = q.shape
-    cc = c - c.min(0).values
-    bc = cc // torch.tensor(block)
-    keys, inv = torch.unique(bc, dim=0, return_inverse=True)        # blocks present
-    pool = torch.zeros(keys.shape[0], n, dtype=torch.float64)
-    pool[inv, torch.arange(n)] = 1.0
-    pool = pool / pool.sum(1, keepdim=True)
-    loc = (bc[:, None, :] - bc[None, :, :]).abs().amax(-1) <= r       # [N, N]
-    far = (bc[:, None, :] - keys[None, :, :]).abs().amax(-1) > r      # [N, nblk]
-    if not with_summaries:
-        far = torch.zeros_like(far)
-    qt, kt = _rope_torch(q, c, base), _rope_torch(k, c, base)
-    kbar = torch.einsum("bn,nhd->bhd", pool, kt)
-    vbar = torch.einsum("bn,nhd->bhd", pool, v)
-    s = torch.einsum("ihd,jhd->hij", qt, kt) / math.sqrt(d)
-    t = torch.einsum("ihd,bhd->hib", qt, kbar) / math.sqrt(d)
-    s = s.masked_fill(~loc[None], float("-inf"))
-    t = t.masked_fill(~far[None], float("-inf"))
-    p = torch.softmax(torch.cat([s, t], -1), -1)
-    vals = torch.cat([v.transpose(0, 1), vbar.transpose(0, 1)], 1)    # [H, N + nblk, D]
-    return (p @ vals).transpose(0, 1)
+    """q, k, v [N, H, D] fp64 tensors; returns o [N, H, D] of the dense-masked formulation
+    (``tests/dense_ref.py``) with the real cos / sin rotation above."""
+    return dense_masked(q, k, v, c, block, r, lambda x: _rope_torch(x, c, base), with_summaries)
 
 
 @pytest.mark.parametrize("grid,block,r,with_s", [((4, 4, 6), (2, 2, 2), 1, True),
