@@ -158,22 +158,28 @@ typedef struct pack3d_tables {
   int32_t ragged, holes; /* holes: some canonical slot is empty */
 } pack3d_tables;
 
-/* Device bytes needed for the index tables of this batch layout, block shape and
- * radius; 0 if the arguments are invalid.  Without ragged the count follows from the
+/* Plumbing (no passage of the pages defines this call): device bytes needed for the
+ * index tables of this batch layout, block shape and radius; 0 if the arguments are
+ * invalid.  Without ragged the count follows from the
  * token counts (a valid volume has N_v / |b| blocks); with ragged it is sized for
  * packing->max_blocks blocks per volume. */
 size_t pack3d_index_bytes(const pack3d_packing* packing, const int32_t block_shape[3],
                           int32_t local_radius);
 
-/* Ragged geometry: the number of blocks per volume (the largest over the batch) that the
- * coordinates need, i.e. the product over the axes of ceil(extent / b), into
+/* Plumbing for ragged geometry (no passage defines this call; it sizes the tables of the
+ * reading of packed geometric data above): the number of blocks per volume (the largest
+ * over the batch) that the coordinates need, i.e. the product over the axes of ceil(extent / b), into
  * *max_blocks_out.  scratch_dev: device buffer of at least 64 * batch bytes.  Runs on the
  * stream and synchronizes it once.  PACK3D_E_COORDS for an empty volume. */
 pack3d_status pack3d_measure_blocks(const int32_t* coords_dev, const pack3d_packing* packing,
                                     const int32_t block_shape[3], void* scratch_dev,
                                     size_t scratch_bytes, void* stream, int32_t* max_blocks_out);
 
-/* Build the index of a batch of packed volumes.
+/* Build the index of a batch of packed volumes ("Geometry Matters in Packed 3D Attention",
+ * abstract: the operator separates memory layout from attention geometry, so locality and
+ * the contiguous 3D blocks are derived from the tokens' true grid coordinates, never from
+ * their packed positions; the tables are therefore the same, up to the packing
+ * permutation, under any repacking).
  *   coords_dev [T, 3] int32 (z, y, x) grid coordinates in packed order.
  *   block_shape (bz, by, bx) >= 1 with bz*by*bx a multiple of 8; local_radius r in
  *   block units (0 <= r <= 7): a query's local set is every key whose block is within
@@ -192,21 +198,29 @@ pack3d_status pack3d_build_index(const int32_t* coords_dev, const pack3d_packing
                                  void* tables_dev, size_t tables_bytes, void* stream,
                                  pack3d_index** out);
 
-/* Fill *out with device views of the tables and their sizes. */
+/* Plumbing (no passage defines this call): fill *out with device views of the tables
+ * and their sizes. */
 pack3d_status pack3d_index_tables(const pack3d_index* index, pack3d_tables* out);
 
-/* Host copy of one volume's origin and extent: out6 = (oz, oy, ox, ez, ey, ex) (the extent
+/* Plumbing (no passage defines this call): host copy of one volume's origin and extent: out6 = (oz, oy, ox, ez, ey, ex) (the extent
  * of the coordinates' bounding box). */
 pack3d_status pack3d_index_geometry(const pack3d_index* index, int32_t volume, int32_t out6[6]);
 
+/* Plumbing (no passage defines this call): release a handle (NULL is ignored); the caller
+ * still owns tables_dev. */
 void pack3d_index_free(pack3d_index* index);
 
-/* Device workspace bytes for pack3d_forward (for_backward = 0) or pack3d_backward
- * (for_backward = 1); 0 if the request is invalid or unsupported. */
+/* Plumbing (no passage defines this call): device workspace bytes for pack3d_forward
+ * (for_backward = 0) or pack3d_backward (for_backward = 1); 0 if the request is invalid
+ * or unsupported. */
 size_t pack3d_workspace_bytes(const pack3d_index* index, const pack3d_attn* attn, int for_backward);
 
-/* Forward.  Writes out [T, H, D] (attn->dtype) and lse [B, H, Nmax] fp32: lse is the
- * natural-log log-sum-exp of the scaled local and summary logits of each query.
+/* Forward ("Geometry Matters in Packed 3D Attention", abstract: local neighbourhood
+ * attention is kept exact, only distant context is compressed into contiguous 3D block
+ * summaries, every query-key and query-summary logit carries axial RoPE on the true grid
+ * coordinates, and the rotation is applied before a block is summarized; local and summary
+ * logits share one softmax).  Writes out [T, H, D] (attn->dtype) and lse [B, H, Nmax] fp32:
+ * lse is the natural-log log-sum-exp of the scaled local and summary logits of each query.
  * coords_dev must hold the coordinates the index was built from: the RoPE angles
  * are taken from them (relative to each volume's origin, which leaves every logit
  * unchanged).  Mismatched coordinates give unspecified values but no out-of-bounds
@@ -218,7 +232,8 @@ pack3d_status pack3d_forward(const pack3d_index* index, const pack3d_attn* attn,
                              const int32_t* coords_dev, void* out_dev, float* lse_dev,
                              void* workspace_dev, size_t workspace_bytes, void* stream);
 
-/* Backward of sum(out * dout): gradients dq, dk, dv [T, H, D] (attn->dtype) with
+/* Backward ("Geometry Matters in Packed 3D Attention", abstract: the operator is
+ * trainable at scale) of sum(out * dout): gradients dq, dk, dv [T, H, D] (attn->dtype) with
  * respect to the unrotated q, k, v, through the RoPE and the block mean pooling (a
  * block's mean spreads 1/n_b to each of its n_b present tokens).
  * out_dev and lse_dev are the forward's outputs for the same inputs.  The workspace
@@ -255,8 +270,8 @@ pack3d_status pack3d_backward_qkv(const pack3d_index* index, const pack3d_attn* 
                                   const void* dout_dev, void* dqkv_dev, void* workspace_dev,
                                   size_t workspace_bytes, int32_t reuse_forward, void* stream);
 
-/* Where the forward leaves its intermediates inside the workspace (byte offsets),
- * for inspection by tests.  All arrays are in canonical order (block-major, raster
+/* Plumbing (no passage defines this call): where the forward leaves its intermediates
+ * inside the workspace (byte offsets), for inspection by tests.  All arrays are in canonical order (block-major, raster
  * inside each block; empty slots hold zero rows), elements of attn->dtype except
  * rope_table (float2 cos, sin).  N below is nblk * |b| canonical rows per volume.
  *   rope_table [extent_table, P]     cos and sin of angle row r, pair k; P = D/6 pairs per
@@ -264,7 +279,9 @@ pack3d_status pack3d_backward_qkv(const pack3d_index* index, const pack3d_attn* 
  *                                    single row 0 (no rotation)
  *   qrot, krot, vrow [B, H, N, Dp]   rotated Q and K, and V, rows zero-padded to Dp
  *   kbar, vbar [B, H, nblk_pad, Dp]  block means (over present tokens) of the rotated K and
- *                                    of V (zero rows for empty and padding blocks)
+ *                                    of V (zero rows for empty and padding blocks); written
+ *                                    only with with_summaries = 1 (the windowed-only
+ *                                    attention reads no block means)
  * Axial rotation angles use coordinates relative to each volume's origin (rows =
  * extents); packed 1D angles use the local packed position (rows = Nmax). */
 typedef struct pack3d_views {
@@ -274,7 +291,7 @@ typedef struct pack3d_views {
 pack3d_status pack3d_workspace_views(const pack3d_index* index, const pack3d_attn* attn,
                                      pack3d_views* out);
 
-/* Kernel timing, for measurement.  While enabled, every kernel launch made by
+/* Kernel timing, for measurement (plumbing; no passage defines these calls).  While enabled, every kernel launch made by
  * pack3d_forward / pack3d_backward is bracketed by two HIP events recorded on the
  * caller's stream (the stream the kernel runs on).  pack3d_profile_read waits for
  * the recorded events, folds them into per-kernel totals and returns, for up to
@@ -287,10 +304,11 @@ int32_t pack3d_profile_read(char* names, size_t names_bytes, int32_t* launches, 
                             int32_t max_kernels);
 void pack3d_profile_reset(void);
 
-/* Thread-local message describing the last error (empty string if none). */
+/* Plumbing (no passage defines these calls): thread-local message describing the last
+ * error (empty string if none), and the ABI version. */
 const char* pack3d_last_error(void);
 
-/* ABI version (major * 100 + minor). */
+/* major * 100 + minor */
 int32_t pack3d_version(void);
 
 #ifdef __cplusplus

@@ -159,3 +159,64 @@ def test_fused_entry_points_argument_errors():
     assert st == p3.E_UNSUPPORTED and b"16 bytes" in lib.pack3d_last_error()
     st = lib.pack3d_forward_qkv(None, None, ctypes.c_void_p(256), None, None, None, None, 0, None)
     assert st == p3.E_INVALID
+
+
+ABI_C = os.path.join(ROOT, "tests", "abi", "abi_consumer.c")
+
+
+def _gcc(out, *extra):
+    import subprocess
+    cmd = ["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), ABI_C, "-o", out, *extra]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _run(exe, *args):
+    import subprocess
+    r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    return dict(line.split(" ", 1) for line in r.stdout.strip().splitlines())
+
+
+def test_c_layout_matches_the_binding(tmp_path):
+    """The header compiled by a C compiler lays out every struct and enum exactly as the
+    ctypes declarations of the binding assume."""
+    exe = str(tmp_path / "abi_layout")
+    _gcc(exe)
+    got = _run(exe)
+    structs = {"pack3d_packing": p3.Packing, "pack3d_attn": p3.Attn, "pack3d_tables": p3.Tables,
+               "pack3d_views": p3.Views}
+    for cname, cls in structs.items():
+        assert int(got[f"sizeof.{cname}"]) == ctypes.sizeof(cls), cname
+        fields = [f[0] for f in cls._fields_]
+        c_fields = sorted(k.split(".")[2] for k in got if k.startswith(f"offsetof.{cname}."))
+        assert sorted(fields) == c_fields, cname
+        for f in fields:
+            assert int(got[f"offsetof.{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
+    enums = {"PACK3D_OK": p3.OK, "PACK3D_E_INVALID": p3.E_INVALID, "PACK3D_E_COORDS": p3.E_COORDS,
+             "PACK3D_E_UNSUPPORTED": p3.E_UNSUPPORTED, "PACK3D_E_WORKSPACE": p3.E_WORKSPACE,
+             "PACK3D_E_HIP": p3.E_HIP, "PACK3D_F32": p3.F32, "PACK3D_BF16": p3.BF16,
+             "PACK3D_ORDER_ANY": p3.ORDERS["any"], "PACK3D_ORDER_RASTER": p3.ORDERS["raster"],
+             "PACK3D_ORDER_MORTON": p3.ORDERS["morton"], "PACK3D_ORDER_BLOCK_CONTIGUOUS": p3.ORDERS["block"],
+             "PACK3D_ORDER_RANDOM": p3.ORDERS["random"], "PACK3D_POS_AXIAL": p3.POSITION_MODES["axial"],
+             "PACK3D_POS_PACKED_1D": p3.POSITION_MODES["packed1d"], "PACK3D_POS_NONE": p3.POSITION_MODES["none"]}
+    c_enums = {k.split(".", 1)[1] for k in got if k.startswith("enum.")}
+    assert c_enums == set(enums)
+    for name, value in enums.items():
+        assert int(got[f"enum.{name}"]) == value, name
+
+
+def test_c_program_links_and_calls_the_library(tmp_path):
+    """A C program linked against libpack3d.so calls the entry points that need no GPU and
+    gets the same answers as the binding."""
+    p3.load_library()
+    libdir = os.path.dirname(p3.LIB_PATH)
+    exe = str(tmp_path / "abi_call")
+    _gcc(exe, "-DPACK3D_LINKED", "-L", libdir, "-lpack3d", f"-Wl,-rpath,{libdir}")
+    got = _run(exe, "call")
+    assert int(got["call.version"]) == p3.load_library().pack3d_version()
+    assert int(got["call.index_bytes"]) == p3.index_bytes(2, 65536, (4, 4, 4), 1) > 0
+    assert int(got["call.index_bytes_bad"]) == 0
+    assert int(got["call.build_index_null"]) == p3.E_INVALID
+    assert got["call.build_index_null_message"] == "set"
+    assert got["call.handle_null"] == "1"
