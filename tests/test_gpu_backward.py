@@ -68,6 +68,30 @@ def test_backward_65k_training_workload_one_head():
         assert torch.isfinite(g).all(), name
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_256_token_blocks_with_summaries_full(dtype):
+    """256-token blocks (4x8x8) on a 4x4x4 block grid, so at r = 1 every query has both
+    local keys (up to 27 blocks of four 64-row tiles) and summaries: the multi-tile cursor
+    paths of the key-major and summary-major backward kernels.  Forward and every gradient
+    element by element against the oracle."""
+    w = si.small_workload(grid=(16, 32, 32), block=(4, 8, 8), radius=1, heads=2, head_dim=96, packing="random",
+                          seed=29)
+    say(f"256-token blocks with summaries {dtype}")
+    x = si.make_inputs(w, dtype, with_grad=True)
+    xd = to_dev(x)
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    out, lse = p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], rope_base=w.rope_base)
+    grads = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], x["coords"], w.block, w.radius)
+    assert max_err(out, o_ref) < TOL[dtype] and max_err(lse, l_ref) < TOL[dtype]
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["coords"], x["do"], w.block, w.radius)
+    for name, g, rr in zip(("dq", "dk", "dv"), grads, ref):
+        err = max_err(g, rr)
+        say(f"  {name}: max err {err:.3e}")
+        assert err < TOL[dtype], (name, err)
+
+
 def test_backward_524k_sampled_dq_and_identities():
     """The 524k workload: one volume of 32x128x128 tokens in 256-token blocks (4x8x8), so each
     block is four 64-query tiles and a query sees up to 6,912 local keys and 2,025 summaries.
@@ -222,3 +246,29 @@ def test_backward_errors():
     torch.cuda.synchronize()
     assert st == p3.E_INVALID and b"16-byte aligned" in lib.pack3d_last_error()
     assert torch.count_nonzero(g) == 0
+
+
+@pytest.mark.timeout(900)
+def test_backward_524k_one_head_elementwise():
+    """The 524k workload at full size (the launch the benchmark would make): every
+    gradient of one head, element by element, against the oracle.  Heads are independent,
+    so the oracle runs on that head's slice of q, k, v and dO."""
+    w = si.WORKLOADS["524k"]
+    dtype = torch.bfloat16
+    head = 6
+    say("backward 524k, one head element-wise")
+    x = si.make_inputs(w, dtype, with_grad=True)
+    xd = to_dev(x)
+    ix = p3.build_index(xd["coords"], w.block, w.radius)
+    out, lse = p3.forward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], rope_base=w.rope_base)
+    grads = p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    got = [g[:, :, head:head + 1].float().cpu().double().numpy() for g in grads]
+    del xd, out, lse, grads
+    one = {n: x[n][:, :, head:head + 1].contiguous() for n in ("q", "k", "v", "do")}
+    say("  oracle backward of one head")
+    ref = oracle.backward(one["q"], one["k"], one["v"], x["coords"], one["do"], w.block, w.radius)
+    for name, g, rr in zip(("dq", "dk", "dv"), got, ref):
+        err = float(np.abs(g - rr).max())
+        say(f"  {name}: max err {err:.3e}")
+        assert err < TOL[dtype], (name, err)
