@@ -226,6 +226,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-sample-blocks", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true", help="skip the hipBLASLt GEMM reference")
+    ap.add_argument("--profile-pass", choices=["step", "forward", "windowed"], default=None,
+                    help="only run warmup + steps of one pass (the step, the forward, or the windowed-only "
+                         "forward) and print its time: for profiler runs, so each pass has its own rows")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args(argv)
@@ -287,10 +290,29 @@ def main(argv=None) -> int:
             p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws,
                         reuse_forward=True, position_mode=pm or mode)
 
+    if args.profile_pass:
+        fn = {"step": step, "forward": fwd, "windowed": lambda: fwd(False)}[args.profile_pass]
+        for _ in range(args.warmup):
+            fn()
+        ms = time_region(fn, args.steps)
+        print(json.dumps({"profile_pass": args.profile_pass, "ms": ms, "steps": args.steps,
+                          "warmup": args.warmup, "workload": args.workload,
+                          "kernel_source_hash": kernel_source_hash()}), flush=True)
+        return 0
+
     for _ in range(args.warmup):
         step()
     log(f"bench: warmup done ({args.warmup} steps), timing {args.steps} steps")
     ms_step = time_region(step, args.steps)
+    # the same steps timed one by one with events on the launch stream (median beside the mean)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    ms_step_median = per_step[len(per_step) // 2]
 
     # same steps again with per-kernel HIP events (library-side, on the launch stream)
     p3.profile_reset()
@@ -402,6 +424,7 @@ def main(argv=None) -> int:
         "windowed_attn": {"avg_ms": win_attn_ms, "tflops": work["attn_fwd_windowed"][0] / (win_attn_ms * 1e-3) / 1e12},
         "index_build_ms": index_ms,
         "ms_per_step_with_kernel_events": ms_step_profiled,
+        "ms_per_step_median_of_events": ms_step_median,
         "pairs_per_volume_head": {"local": local, "summary": summ},
         "kernel_source_hash": kernel_source_hash(),
     }
