@@ -8,14 +8,19 @@ one summary per distant block) reduces on: a volume that is a single block (no
 summaries), a radius that covers the whole block grid (dense attention), and volumes one
 token thick along one or two axes.
 
-At the block-count maximum the oracle computes o, lse and dq on sampled query blocks;
-dk and dv need every query there, so they are held to two exact identities of the
-method instead (each query's weights over keys and summaries sum to one, and a block
-mean hands a summary's gradient to its members in full):
+At the block-count maximum the oracle computes o, lse and dq on sampled query blocks.
+dk and dv need every query there (minutes of fp64 work per head), so the oracle's
+gradients of one head on the tokens of sampled blocks are stored by
+tests/golden/make_limit_gradients.py and compared element by element, and over all
+tokens dk and dv are held to two exact identities of the method (each query's weights
+over keys and summaries sum to one, and a block mean hands a summary's gradient to its
+members in full):
     sum_j dv_j = sum_i dO_i            and        sum_j R_j dk_j = 0
 per (volume, head, channel), R_j the token's rotation.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -30,6 +35,7 @@ from tests.gpu_cases import DEV, TOL, max_err, sample_blocks, say, to_dev
 pytestmark = pytest.mark.gpu
 
 MAX_BLOCKS = 16384
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "limit_gradients.json")
 
 
 def _run(w, x, with_summaries=True):
@@ -76,6 +82,19 @@ def test_maximum_blocks_per_volume(dtype, heads, d):
     assert max_err(dq, dq_ref, qmask) < TOL[dtype]
     for g in (out, lse, dq, dk, dv):
         assert torch.isfinite(g).all()
+    # every gradient of one head element by element on the tokens of sampled blocks, against
+    # the oracle's values stored by tests/golden/make_limit_gradients.py (minutes of fp64 work
+    # per head, run once on the CPU)
+    golden = json.load(open(GOLDEN))
+    assert tuple(golden["grid"]) == w.grid and tuple(golden["block"]) == w.block and golden["seed"] == w.seed
+    case = golden["cases"]["fp32_d12" if dtype == torch.float32 else "bf16_d96"]
+    assert (case["heads"], case["head_dim"]) == (heads, d)
+    h, tok = case["head"], torch.tensor(case["tokens"])
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        got = g[0][tok.to(DEV), h].double().cpu().numpy()
+        err = float(np.abs(got - np.asarray(case[name])).max())
+        say(f"  {name} on {len(tok)} stored tokens of head {h}: max err {err:.3e}")
+        assert err < TOL[dtype], (name, err)
     # identities for dk and dv over all 131072 tokens
     do64 = x["do"][0].double()
     scale = do64.abs().sum(0)                                            # [H, D]
