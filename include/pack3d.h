@@ -270,6 +270,26 @@ pack3d_status pack3d_backward_qkv(const pack3d_index* index, const pack3d_attn* 
                                   const void* dout_dev, void* dqkv_dev, void* workspace_dev,
                                   size_t workspace_bytes, int32_t reuse_forward, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): pack3d_forward with the workspace
+ * taken from a fixed device buffer the library holds, PACK3D_NOALLOC_MAX_BYTES (128 MiB)
+ * on every GPU it runs on, kept until the process ends.  Arguments, results and errors
+ * are those of pack3d_forward (bitwise equal results); there is no workspace argument.
+ * The call allocates nothing: no hipMalloc / hipFree, no host allocation, no HIP events
+ * (kernel timing records nothing during it).  Its first call on a device, with that device
+ * current, looks up the buffer's address there (hipGetSymbolAddress) and keeps it.
+ * Returns PACK3D_E_WORKSPACE, before any launch, when the forward needs more than
+ * PACK3D_NOALLOC_MAX_BYTES of workspace (pack3d_workspace_bytes(index, attn, 0)).  Every
+ * call on one GPU shares that GPU's buffer: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give wrong results; calls on one stream are
+ * ordered and safe.  The buffer keeps the last call's contents; nothing in it needs to
+ * start at zero. */
+#define PACK3D_NOALLOC_MAX_BYTES ((size_t)128 << 20)
+pack3d_status pack3d_forward_noalloc(const pack3d_index* index, const pack3d_attn* attn,
+                                     const void* q_dev, const void* k_dev, const void* v_dev,
+                                     const int32_t* coords_dev, void* out_dev, float* lse_dev,
+                                     void* stream);
+
 /* Plumbing (no passage defines this call): where the forward leaves its intermediates
  * inside the workspace (byte offsets), for inspection by tests.  All arrays are in canonical order (block-major, raster
  * inside each block; empty slots hold zero rows), elements of attn->dtype except

@@ -2,8 +2,16 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "layout.h"
+
+// Device scratch of pack3d_forward_noalloc: the forward's workspace for callers that cannot
+// allocate.  Every GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory: kernels get the
+// address hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static constexpr size_t kNoAllocBytes = PACK3D_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
 
 namespace pack3d {
 
@@ -133,6 +141,31 @@ pack3d_status run_backward(const pack3d_index* ix, const pack3d_attn* at, const 
   return launch_attn_bwd(d, ix, at, coords, out, lse, dout, dq, dk, dv, (char*)ws, w, s);
 }
 
+// Device address of `scratch` on the current device, taken once per device with that
+// device current and kept; later calls reuse it.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+pack3d_status noalloc_scratch(void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(PACK3D_E_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(PACK3D_E_UNSUPPORTED, "%s: device %d is beyond the %d devices supported", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(PACK3D_E_HIP, "%s: hipGetSymbolAddress of the scratch buffer on device %d: %s", who, dev,
+                       hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return PACK3D_OK;
+}
+
 // The fused [T, 3, H, D] layout needs every head block (H * D elements) to start on a
 // 16-byte boundary.
 pack3d_status check_fused(const pack3d_attn* at, const char* who) {
@@ -151,6 +184,26 @@ extern "C" pack3d_status pack3d_forward(const pack3d_index* ix, const pack3d_att
                                         float* lse, void* ws, size_t ws_bytes, void* stream) {
   const int64_t hd = at ? (int64_t)at->heads * at->head_dim : 0;
   return run_forward(ix, at, q, k, v, coords, out, lse, ws, ws_bytes, hd, stream, "forward");
+}
+
+extern "C" pack3d_status pack3d_forward_noalloc(const pack3d_index* ix, const pack3d_attn* at, const void* q,
+                                                const void* k, const void* v, const int32_t* coords, void* out,
+                                                float* lse, void* stream) {
+  const char* who = "forward_noalloc";
+  pack3d_status st = check_attn(ix, at, who);
+  if (st != PACK3D_OK) return st;
+  const size_t need = workspace_layout(make_dims(ix, at)).fwd_total;
+  if (need > kNoAllocBytes)
+    return set_error(PACK3D_E_WORKSPACE,
+                     "%s: this forward needs %zu bytes of workspace, more than the %zu bytes of the fixed device "
+                     "scratch buffer; call pack3d_forward with a caller workspace instead",
+                     who, need, kNoAllocBytes);
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws, who);
+  if (st != PACK3D_OK) return st;
+  ProfileOff quiet;  // kernel timing would create events
+  const int64_t hd = (int64_t)at->heads * at->head_dim;
+  return run_forward(ix, at, q, k, v, coords, out, lse, ws, kNoAllocBytes, hd, stream, who);
 }
 
 extern "C" pack3d_status pack3d_backward(const pack3d_index* ix, const pack3d_attn* at, const void* q,

@@ -27,6 +27,13 @@ struct ProfileScope {
   hipStream_t stream;
 };
 
+// While one is alive on a thread, ProfileScope records nothing on that thread (no events
+// are created and no host memory is taken), whatever pack3d_profile_enable says.
+struct ProfileOff {
+  ProfileOff();
+  ~ProfileOff();
+};
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Geometry record per volume, stored in device memory as int32[G_FIELDS]: origin,

@@ -22,6 +22,7 @@ struct Totals {
 
 std::mutex g_mu;
 bool g_enabled = false;
+thread_local int g_off = 0;  // ProfileOff scopes alive on this thread
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_free;
 std::vector<Totals> g_totals;
@@ -39,7 +40,11 @@ hipEvent_t take_event() {
 
 }  // namespace
 
+ProfileOff::ProfileOff() { ++g_off; }
+ProfileOff::~ProfileOff() { --g_off; }
+
 ProfileScope::ProfileScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  if (g_off) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_enabled) return;
   Pending p;

@@ -79,6 +79,8 @@ EXPORTS = {
                            + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pack3d_backward_qkv": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 6
                             + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]),
+    "pack3d_forward_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn)] + [ctypes.c_void_p] * 6
+                               + [ctypes.c_void_p]),
     "pack3d_workspace_views": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Attn), ctypes.POINTER(Views)]),
     "pack3d_profile_enable": (ctypes.c_int, [ctypes.c_int32]),
     "pack3d_profile_read": (ctypes.c_int32, [ctypes.c_char_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
@@ -336,6 +338,28 @@ def forward(index: Index, q, k, v, coords, *, rope_base=10000.0, scale=None, wit
                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                   ctypes.c_void_p(_stream())))
     return out, lse
+
+
+def forward_noalloc(index: Index, q, k, v, coords, out, lse, *, rope_base=10000.0, scale=None,
+                    with_summaries=True, position_mode="axial"):
+    """The forward for callers that cannot allocate: the library's fixed device buffer is the
+    workspace (at most NOALLOC_MAX_BYTES) and the caller passes ``out`` and ``lse``; results
+    are bitwise those of ``forward``.  Calls that overlap on one GPU race on that buffer."""
+    lib = load_library()
+    h, d = q.shape[-2], q.shape[-1]
+    attn = make_attn(q.dtype, h, d, rope_base, scale, with_summaries, position_mode)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_act(name, t, index.act_shape(h, d), q.dtype)
+    _check_coords(index, coords)
+    _check_lse(index, lse, h)
+    _check_device(index, q, k, v, coords, out, lse)
+    with torch.cuda.device(index.device):
+        _check(lib.pack3d_forward_noalloc(index.handle, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(coords),
+                                          _ptr(out), _ptr(lse), ctypes.c_void_p(_stream())))
+    return out, lse
+
+
+NOALLOC_MAX_BYTES = 128 << 20   # PACK3D_NOALLOC_MAX_BYTES of include/pack3d.h
 
 
 def backward(index: Index, q, k, v, coords, out, lse, dout, *, rope_base=10000.0, scale=None,

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     lib = p3.load_library()
     names = _declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) <= set(p3.EXPORTS)
