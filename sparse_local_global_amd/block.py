@@ -22,12 +22,13 @@ from .pack3d import Index, attention_qkv
 
 class Pack3DBlock(torch.nn.Module):
     def __init__(self, dim: int, heads: int, mlp_ratio: int = 4, rope_base: float = 10000.0,
-                 device=None, dtype=None):
+                 device=None, dtype=None, position_mode: str = "axial"):
         super().__init__()
         if dim % heads:
             raise ValueError("dim must be a multiple of heads")
         kw = dict(device=device, dtype=dtype)
         self.dim, self.heads, self.rope_base = dim, heads, rope_base
+        self.position_mode = position_mode  # rotation of the operator (see pack3d.make_attn)
         self.norm1 = torch.nn.LayerNorm(dim, eps=1e-5, **kw)
         self.qkv = torch.nn.Linear(dim, 3 * dim, bias=False, **kw)
         self.proj = torch.nn.Linear(dim, dim, bias=False, **kw)
@@ -51,7 +52,7 @@ class Pack3DBlock(torch.nn.Module):
         t = x.shape[0]
         d = self.dim // self.heads
         qkv = self.qkv(self.norm1(x)).view(t, 3, self.heads, d)
-        a = attention_qkv(qkv, index, coords, rope_base=self.rope_base)
+        a = attention_qkv(qkv, index, coords, rope_base=self.rope_base, position_mode=self.position_mode)
         x1 = x + self.proj(a.view(t, self.dim))
         y = x1 + self.fc2(torch.nn.functional.gelu(self.fc1(self.norm2(x1))))
         return y.view(shape)
