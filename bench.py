@@ -269,7 +269,8 @@ def main(argv=None) -> int:
     out = torch.empty_like(xd["q"])
     lse = torch.empty((w.batch, w.heads, w.tokens), dtype=torch.float32, device="cuda:0")
 
-    with_bwd = not args.forward_only
+    # a profiler pass over the forward alone launches no backward kernel at all
+    with_bwd = not args.forward_only and args.profile_pass not in ("forward", "windowed")
     if with_bwd:
         try:
             p3.backward(ix, xd["q"], xd["k"], xd["v"], xd["coords"], out, lse, xd["do"], workspace=ws,
