@@ -1095,6 +1095,234 @@ void k_bwd_dq(BwdArgs a) {
   write_rows<T>(a, &sm.u.st[0][0], DP + 1, nq, b, h, qrow0, true, (T*)a.dq, sm.src, sm.rel);
 }
 
+// ---------------------------------------------------------------------------------
+// bwd_dq for bf16 at D = 96 with blocks of 64-token multiples: 32 query columns per wave,
+// fed by direct LDS copies.  Workgroup = (64 queries, head, volume), four waves: query half
+// qh = wave >> 1 (the wave's 32 queries are the B operand, in registers) and key half
+// kh = wave & 1 of every key tile.  Per tile a wave forms S^T = K Q^T and dP^T = V dO^T - delta
+// for its 32 keys (v_mfma_f32_32x32x16_bf16), dS = P * dP, and dQ^T += K^T dS^T with K read
+// transposed.  The 32x32 products read half the LDS bytes per multiply of the 16-column
+// kernel, which is bound by LDS bandwidth.  K and V tiles arrive by direct copies into two
+// stages (separate LDS objects, so plain reads of one stage do not wait for copies into the
+// other); the transposed K operands are read by one asm block that waits only for its own
+// reads.  The two key halves' partial dQ are added through LDS before the epilogue.
+// ---------------------------------------------------------------------------------
+constexpr int kDq32LiveTiles = 32;
+
+struct DqSmem32 {
+  int list[kMaxSlots];
+  uint32_t mask[kMaxBlocks / 32];
+  uint64_t live[kDq32LiveTiles];  // local tile t: bit r = key row r holds a token (empty slots only)
+  int nloc;
+};
+
+template <int DP>
+struct DqStage32 {
+  RowTile<bf16, DP> k, v;
+};
+
+// Epilogue for D = 96: lane (query col, half h) holds dims 32dt + 8(i/4) + 4h + i%4 in slot i
+// of block dt, so each rotation pair (k, k + 16 of an axis group; k, k + 48 in 1D) sits in one
+// lane; dq = R^T (scale * acc) is stored as 8-byte pieces.
+__device__ inline void dq32_epilogue96(const BwdArgs& a, f32x16 (&acc)[3], int b, int h, int row, bool ok,
+                                       int half) {
+  if (!ok) return;
+  const int src = a.perm[(int64_t)b * a.NC + row];
+  if (src < 0) return;  // empty slot
+  const int64_t tok0 = a.voff[b];
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] *= a.scale;
+  if (a.pos_mode == PACK3D_POS_AXIAL) {
+    const int32_t* g = a.geom + b * G_FIELDS;
+    const int32_t* c = a.coords + (tok0 + src) * 3;
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+      int r = c[dt] - g[G_OZ + dt];
+      r = r < 0 ? 0 : (r >= a.trows ? a.trows - 1 : r);
+      const float2* cs = a.tab + (int64_t)r * 16 + 4 * half;  // 16 pairs per axis
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 t = cs[8 * j + e];
+          const float lo = acc[dt][4 * j + e], hi = acc[dt][4 * j + 8 + e];
+          acc[dt][4 * j + e] = lo * t.x + hi * t.y;       // y1 c + y2 s
+          acc[dt][4 * j + 8 + e] = -lo * t.y + hi * t.x;  // -y1 s + y2 c
+        }
+    }
+  } else if (a.pos_mode == PACK3D_POS_PACKED_1D) {
+    const float2* cs = a.tab + (int64_t)src * 48 + 4 * half;  // 48 pairs (k, k + 48) per row
+#pragma unroll
+    for (int m = 0; m < 6; ++m)  // dims 8m + 4 half + e and 8(m + 6) + 4 half + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 t = cs[8 * m + e];
+        const float y1 = acc[m / 4][4 * (m % 4) + e], y2 = acc[(m + 6) / 4][4 * ((m + 6) % 4) + e];
+        acc[m / 4][4 * (m % 4) + e] = y1 * t.x + y2 * t.y;
+        acc[(m + 6) / 4][4 * ((m + 6) % 4) + e] = -y1 * t.y + y2 * t.x;
+      }
+  }
+  bf16* dst = (bf16*)a.dq + (tok0 + src) * a.grad_stride + (int64_t)h * 96;
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *(bf16x4*)(dst + 32 * dt + 8 * jj + 4 * half) =
+          bf16x4{(bf16)acc[dt][4 * jj], (bf16)acc[dt][4 * jj + 1], (bf16)acc[dt][4 * jj + 2], (bf16)acc[dt][4 * jj + 3]};
+}
+
+template <int DP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void k_bwd_dq32(BwdArgs a) {
+  static_assert(DP == 96, "the transposed reads and the epilogue are written for D = 96");
+  __shared__ DqSmem32 sm;
+  __shared__ DqStage32<DP> s0, s1;
+  static_assert(sizeof(f32x4) * (4 * DP / 32) * 64 * 2 <= sizeof(DqStage32<DP>), "partial dq fits a stage");
+  const int ntile = a.nblk * a.tiles_per_block;
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % ntile, h = (L / ntile) % a.H, b = L / ntile / a.H;
+  const int qb = tile / a.tiles_per_block, qs = tile - qb * a.tiles_per_block;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int N = a.NC, bvol = a.bvol;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int qrow0 = qb * bvol + qs * kTile;  // bvol is a multiple of 64: 64 queries per tile
+  const int qloc = 32 * qh + col;
+  const uint32_t* occ = a.occ + (int64_t)b * a.occ_words;
+  if (a.holes && !any_occupied(occ, qrow0, kTile)) return;  // no token among the tile's queries
+  ColFrag32<DP> qf, gf;
+  qf.load((const bf16*)a.qrot + (bh * N + qrow0 + qloc) * DP, true, half);
+  gf.load((const bf16*)a.doc + (bh * N + qrow0 + qloc) * DP, true, half);
+  const float lse2 = a.lsec[bh * N + qrow0 + qloc];   // +inf at an empty slot: P = 0
+  const float ndelta = a.ndelta[bh * N + qrow0 + qloc];
+
+  const int mask_words = a.nblkp / 32;
+  for (int i = tid; i < mask_words; i += kThreads) sm.mask[i] = a.holes ? a.emask[(int64_t)b * mask_words + i] : 0u;
+  if (wave == 0) compact_neighbours(a.nbr + ((int64_t)b * a.nblk + qb) * a.slots, a.slots, sm.list, &sm.nloc);
+  __syncthreads();
+  const int nloc = __builtin_amdgcn_readfirstlane(sm.nloc);
+  for (int i = tid; i < nloc; i += kThreads) atomicOr(&sm.mask[sm.list[i] >> 5], 1u << (sm.list[i] & 31));
+  const int nkeys = nloc * bvol;
+  const int nlt = nkeys / kTile;
+  const int total = nlt + (a.with_summaries ? a.nblkp / kTile : 0);
+  // with empty slots the local tiles' occupancy is read before any copy is in flight
+  const bool live_table = a.holes && nlt <= kDq32LiveTiles;
+  if (live_table) {
+    for (int t = wave; t < nlt; t += kThreads / 64) {
+      const uint64_t lv = occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), kTile);
+      if (lane == 0) sm.live[t] = lv;
+    }
+  }
+  wait_vm<0>();  // the query rows, lse and delta are in registers before any copy starts
+  f32x16 dq[DP / 32];
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) dq[dt] = f32x16{};
+  const float c = a.scale_log2;
+
+  const size_t es = sizeof(bf16);
+  const bf16* kq = (const bf16*)a.krot + bh * N * DP;
+  const bf16* vq = (const bf16*)a.vr + bh * N * DP;
+  const bf16* kbq = (const bf16*)a.kbar + bh * a.nblkp * DP;
+  const bf16* vbq = (const bf16*)a.vbar + bh * a.nblkp * DP;
+  const size_t bytes_loc = (size_t)N * DP * es, bytes_sum = (size_t)a.nblkp * DP * es;
+  using Dma = TileDma<DP, kThreads>;
+  const Dma dma;
+  auto stage = [&](auto sg) -> DqStage32<DP>& {
+    if constexpr (decltype(sg)::value == 0) return s0;
+    else return s1;
+  };
+  // tiles are issued in order, so a cursor (entry of the neighbour list, 64-row tile within
+  // that block) replaces a division per tile
+  const int tpb = a.tiles_per_block;
+  int cur_entry = 0, cur_sub = 0;
+  auto issue = [&](DqStage32<DP>& S, int t) {
+    const bool loc = t < nlt;
+    uint32_t row0 = (uint32_t)(t - nlt) * kTile;
+    if (loc) {
+      const int blk = __builtin_amdgcn_readfirstlane(sm.list[cur_entry]);
+      row0 = (uint32_t)(blk * bvol + cur_sub * kTile);
+      if (++cur_sub == tpb) {
+        cur_sub = 0;
+        ++cur_entry;
+      }
+    }
+    const size_t bytes = loc ? bytes_loc : bytes_sum;
+    const Src ks(loc ? kq : kbq, bytes), vs(loc ? vq : vbq, bytes);
+    // (issue_at here would cost another kernel's host-side stub, see bwd_local32; the row
+    // form with every row valid copies the same bytes)
+    dma.issue(ks, S.k, kTile, [&](int r) { return (int)(row0 + r) * DP; });
+    dma.issue(vs, S.v, kTile, [&](int r) { return (int)(row0 + r) * DP; });
+  };
+  // this wave's live key rows of tile t (bit r: row 32kh + r)
+  auto live_rows = [&](int t) -> uint32_t {
+    uint64_t live;
+    if (t < nlt) {
+      live = a.holes ? (live_table ? sm.live[t] : occupied_rows(occ, VirtualRows(sm.list, bvol, t * kTile), kTile))
+                     : ~0ull;
+    } else {
+      const int ts = t - nlt, r0 = ts * kTile;
+      const int rows = a.nblk - r0 < kTile ? a.nblk - r0 : kTile;
+      const uint64_t used = ((uint64_t)sm.mask[2 * ts + 1] << 32) | sm.mask[2 * ts];
+      live = (rows >= 64 ? ~0ull : ((1ull << rows) - 1ull)) & ~used;
+    }
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(kh ? (uint32_t)(live >> 32) : (uint32_t)live));
+  };
+  auto compute = [&](auto sg, uint32_t mine) {
+    const DqStage32<DP>& S = stage(sg);
+    // S^T and dP^T for keys 32kh .. 32kh+31; dS = P (dP - delta), with -delta added here (a
+    // register block of it as the accumulators' start would stay live across the loop)
+    f32x16 s, dp;
+    score32_pair(S.k, qf, s, S.v, gf, dp, col, half, kh);
+    if (mine != ~0u) mask_rows32(s, mine, half);
+    bf16x8 pb[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p0 = fast_exp2(fmaf(s[2 * j], c, -lse2)), p1 = fast_exp2(fmaf(s[2 * j + 1], c, -lse2));
+      pb[j >> 2][2 * (j & 3)] = (bf16)(p0 * (dp[2 * j] + ndelta));
+      pb[j >> 2][2 * (j & 3) + 1] = (bf16)(p1 * (dp[2 * j + 1] + ndelta));
+    }
+    RowsFrag32<DP> kfr;
+    read_rows32_96(S.k, kfr, lane, half, kh);  // this stage landed; copies in flight target the other
+    accum32_packed(kfr, pb, dq);
+  };
+  auto step = [&](auto sg, int t) {
+    constexpr int SI = decltype(sg)::value;
+    wait_vm<0>();
+    barrier_copies();  // tile t is in stage SI; every wave is done with the other stage
+    const uint32_t mine = live_rows(t);
+    if (t + 1 < total) issue(stage(Stage_<1 - SI>{}), t + 1);
+    if (mine) compute(sg, mine);
+  };
+  if (total > 0) issue(s0, 0);
+  for (int t = 0; t < total; t += 2) {
+    step(Stage_<0>{}, t);
+    if (t + 1 < total) step(Stage_<1>{}, t + 1);
+  }
+  __syncthreads();  // stage 0 is reused for the key halves' partial dq
+  f32x4* part = (f32x4*)&s0 + qh * (4 * DP / 32) * 64;  // [qh][slot][lane]
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        part[(4 * dt + q) * 64 + lane] = f32x4{dq[dt][4 * q], dq[dt][4 * q + 1], dq[dt][4 * q + 2], dq[dt][4 * q + 3]};
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 o = part[(4 * dt + q) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dq[dt][4 * q + e] += o[e];
+    }
+  dq32_epilogue96(a, dq, b, h, qrow0 + qloc, true, half);
+}
+
 template <typename T, int DP, bool ONE_BLOCK>
 pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   const dim3 tiles(d.nblk * a.tiles_per_block * d.H * d.B);
@@ -1123,7 +1351,15 @@ pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   }
   {
     ProfileScope prof("bwd_dq", s);
-    hipLaunchKernelGGL((k_bwd_dq<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
+    // 32-column waves with direct copies for bf16 at D = 96 in blocks of 64-token multiples;
+    // position mode "none" keeps the register-staged kernel (see the note on earlier
+    // direct-copy attempts in the design notes)
+    if constexpr (sizeof(T) == 2 && DP == 96 && ONE_BLOCK) {
+      if (d.D == 96 && a.pos_mode != PACK3D_POS_NONE) hipLaunchKernelGGL(k_bwd_dq32<96>, tiles, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((k_bwd_dq<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k_bwd_dq<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);
+    }
   }
   return check_launch("backward: attention");
 }

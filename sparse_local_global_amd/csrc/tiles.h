@@ -371,6 +371,60 @@ __device__ inline void read_rows32(const RowTile<bf16, DP>& t, RowsFrag32<DP>& v
     }
 }
 
+// The A operands of accum32_rows for DP = 96 (rows 32mt .. 32mt+31 of tile t), read with the
+// LDS transpose load in one asm block that waits for its own reads before it ends.  The
+// builtin makes the compiler wait for every copy in flight first (it cannot tell LDS stages
+// apart for this load); a caller of this version must itself make sure the tile has landed
+// and that no copy in flight targets it.
+__device__ inline void read_rows32_96(const RowTile<bf16, 96>& t, RowsFrag32<96>& v, int lane, int half, int mt) {
+  using G = TileGeom<bf16, 96>;
+  const int lane16 = lane & 15, hi16 = (lane >> 4) & 1;
+  const ColumnBases c0 = column_bases<96>(4 * half, lane16), c8 = column_bases<96>(8 + 4 * half, lane16);
+  const int p0 = (hi16 ? c0.odd : c0.even) + G::off(32 * mt, 0);
+  const int p8 = (hi16 ? c8.odd : c8.even) + G::off(32 * mt, 0);
+  const uint32_t a0 = (uint32_t)(uintptr_t)(const lds_bf16*)(t.x + p0);
+  const uint32_t a8 = (uint32_t)(uintptr_t)(const lds_bf16*)(t.x + p8);
+  // byte offsets: rows 16 s (s = 0, 1) and column blocks 32 dt (dt = 0, 1, 2): 2 (16 s 96 + 32 dt)
+  v4i16 l00, h00, l01, h01, l02, h02, l10, h10, l11, h11, l12, h12;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12\n\t"
+      "ds_read_b64_tr_b16 %1, %13\n\t"
+      "ds_read_b64_tr_b16 %2, %12 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:64\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:128\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:128\n\t"
+      "ds_read_b64_tr_b16 %6, %12 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %7, %13 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %8, %12 offset:3136\n\t"
+      "ds_read_b64_tr_b16 %9, %13 offset:3136\n\t"
+      "ds_read_b64_tr_b16 %10, %12 offset:3200\n\t"
+      "ds_read_b64_tr_b16 %11, %13 offset:3200\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l00), "=&v"(h00), "=&v"(l01), "=&v"(h01), "=&v"(l02), "=&v"(h02), "=&v"(l10), "=&v"(h10),
+        "=&v"(l11), "=&v"(h11), "=&v"(l12), "=&v"(h12)
+      : "v"(a0), "v"(a8)
+      : "memory");
+  const v4i16 lo[2][3] = {{l00, l01, l02}, {l10, l11, l12}};
+  const v4i16 hi[2][3] = {{h00, h01, h02}, {h10, h11, h12}};
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+      const bf16x4 l = __builtin_bit_cast(bf16x4, lo[s][dt]);
+      const bf16x4 h = __builtin_bit_cast(bf16x4, hi[s][dt]);
+      v.a[s][dt] = bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+    }
+}
+
+// Rows 8(i/4) + 4h + i%4 of a 32x32 score block (slot i, lane half h) whose bit is clear in
+// `mine` become -inf.
+__device__ inline void mask_rows32(f32x16& s, uint32_t mine, int half) {
+  const uint32_t mh = mine >> (4 * half);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (!((mh >> (8 * (i >> 2) + (i & 3))) & 1u)) s[i] = -INFINITY;
+}
+
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // p = exp2(c s - m) for the 16 slots of a 32x32 score block, rounded to bf16 into the B
