@@ -53,6 +53,7 @@ struct RopeArgs {
   void* qrot; void* krot; void* vr; void* kbar; void* vbar;
   int NC, H, D, Dp, nblk, nblkp, bvol, heads_per_group, holes;
   int pool;  // 0: windowed-only attention reads no block means, so none are formed
+  int bz, by, bx;  // block shape: a canonical slot's position in the volume follows from it
   int64_t in_stride;  // elements between consecutive tokens of q, k, v
   int pos_mode, groups, gw, half, trows;  // rotation groups (see Dims)
 };
@@ -69,24 +70,43 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   const int ntok = bvol < kChunk ? bvol : kChunk;  // rows of the staging tiles
   const int nchunk = (bvol + kChunk - 1) / kChunk;   // the last chunk may be partial (|b| = 40, 48, 56)
   const bool pool = a.pool != 0;
-  // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1], vl[ntok][Dp+1] (float)
+  // LDS: src[bvol], rel[bvol][3] (int), kl[ntok][Dp+1], vl[ntok][Dp+1] (the input dtype: the
+  // rotated K as stored, and V, are what the block means average)
   int* s_src = (int*)smem;
   int* s_rel = s_src + bvol;
-  float* kl = (float*)(s_rel + 3 * bvol);
+  T* kl = (T*)(s_rel + 3 * bvol);
   const int ls = Dp + 1;
-  float* vl = kl + ntok * ls;
+  T* vl = kl + ntok * ls;
 
   const int32_t* g = a.geom + b * G_FIELDS;
   const int64_t tok0 = a.voff[b];  // packed token offset of the volume
+  // Axial angle rows: a canonical slot is block blk, offset t inside it, so its position
+  // relative to the volume's origin is beta(blk) * b + w(t), the coordinate minus the origin
+  // the index placed there (no gather of the coordinates).
+  int base[3] = {0, 0, 0};
+  if (GROUPS == 3) {
+    const int nby = (g[G_EY] + a.by - 1) / a.by, nbx = (g[G_EX] + a.bx - 1) / a.bx;
+    base[0] = blk / (nby * nbx) * a.bz;
+    base[1] = (blk / nbx) % nby * a.by;
+    base[2] = blk % nbx * a.bx;
+  }
   for (int t = tid; t < bvol; t += 256) {
     const int kappa = blk * bvol + t;
     const int src = a.perm[(int64_t)b * NC + kappa];  // -1: empty slot
     s_src[t] = src;
-    if (src >= 0) {
-      const int32_t* c = a.coords + (tok0 + src) * 3;
-      for (int gi = 0; gi < GROUPS; ++gi) s_rel[t * 3 + gi] = rope_row(a.pos_mode, gi, src, c, g, a.trows);
-    } else {
-      for (int gi = 0; gi < GROUPS; ++gi) s_rel[t * 3 + gi] = 0;
+    int rel[3] = {0, 0, 0};
+    if (src >= 0 && ROTATE) {
+      if (GROUPS == 3) {
+        rel[0] = base[0] + t / (a.by * a.bx);
+        rel[1] = base[1] + (t / a.bx) % a.by;
+        rel[2] = base[2] + t % a.bx;
+      } else {
+        rel[0] = src;  // packed 1D: the position in the volume
+      }
+    }
+    for (int gi = 0; gi < GROUPS; ++gi) {
+      const int r = rel[gi];
+      s_rel[t * 3 + gi] = r < 0 ? 0 : (r >= a.trows ? a.trows - 1 : r);
     }
   }
   __syncthreads();
@@ -143,8 +163,8 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           ok1.v[e] = from_f<T>(ky1);
           ok2.v[e] = from_f<T>(ky2);
           if (pool) {
-            kl[tok * ls + col1 + e] = ky1;
-            kl[tok * ls + col2 + e] = ky2;
+            kl[tok * ls + col1 + e] = ok1.v[e];
+            kl[tok * ls + col2 + e] = ok2.v[e];
           }
         }
         const int64_t out_row = (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp;
@@ -168,7 +188,7 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
         *(Vec<T, VEC>*)(vr + (bh * NC + (int64_t)blk * bvol + t0 + tok) * Dp + col) = x;
         if (pool) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) vl[tok * ls + col + e] = to_f(x.v[e]);
+          for (int e = 0; e < VEC; ++e) vl[tok * ls + col + e] = x.v[e];
         }
       }
       // zero padding columns D..Dp of the rows and of the staged tiles
@@ -181,8 +201,8 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
           krot[out_row + col] = from_f<T>(0.f);
           vr[out_row + col] = from_f<T>(0.f);
           if (pool) {
-            kl[tok * ls + col] = 0.f;
-            vl[tok * ls + col] = 0.f;
+            kl[tok * ls + col] = from_f<T>(0.f);
+            vl[tok * ls + col] = from_f<T>(0.f);
           }
         }
       }
@@ -190,9 +210,9 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
       __syncthreads();
       // column sums over the chunk: threads 0 .. Dp-1 sum K~ columns, Dp .. 2Dp-1 V columns
       if (tid < 2 * Dp) {
-        const float* col = tid < Dp ? kl + tid : vl + (tid - Dp);
+        const T* col = tid < Dp ? kl + tid : vl + (tid - Dp);
         float cs = 0.f;
-        for (int t = 0; t < cnt; ++t) cs += col[t * ls];
+        for (int t = 0; t < cnt; ++t) cs += to_f(col[t * ls]);
         csum += cs;
       }
       __syncthreads();
@@ -229,7 +249,8 @@ void launch_mode(const Dims& d, const RopeArgs& a, dim3 grid, size_t lds, hipStr
 template <typename T>
 pack3d_status launch_typed(const Dims& d, const RopeArgs& a, const char* name, hipStream_t s) {
   const int ntok = d.bvol < kChunk ? d.bvol : kChunk;
-  const size_t lds = sizeof(int) * 4 * d.bvol + 2 * sizeof(float) * ntok * (d.Dp + 1);
+  // the staging tiles exist only to form the block means
+  const size_t lds = sizeof(int) * 4 * d.bvol + (a.pool ? 2 * sizeof(T) * ntok * (d.Dp + 1) : 0);
   dim3 grid(d.nblk, d.H / a.heads_per_group, d.B);
   ProfileScope prof(name, s);
   if (d.pos_mode == PACK3D_POS_AXIAL) launch_mode<T, 3, true>(d, a, grid, lds, s);
@@ -256,6 +277,7 @@ pack3d_status launch_rope_pool(const Dims& d, const pack3d_index* ix, const pack
   a.qrot = ws + w.qrot; a.krot = ws + w.krot; a.vr = ws + w.vr; a.kbar = ws + w.kbar; a.vbar = ws + w.vbar;
   a.in_stride = d.in_stride;
   a.pool = at->with_summaries ? 1 : 0;
+  a.bz = ix->block[0]; a.by = ix->block[1]; a.bx = ix->block[2];
   a.NC = d.NC; a.H = d.H; a.D = d.D; a.Dp = d.Dp; a.nblk = d.nblk; a.nblkp = d.nblkp; a.bvol = d.bvol;
   a.pos_mode = d.pos_mode; a.groups = d.groups; a.gw = d.gw; a.half = d.half; a.trows = d.trows;
   // heads per workgroup: the fewest whose rows cover whole 128-byte lines, else all
