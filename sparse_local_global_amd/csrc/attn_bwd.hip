@@ -1351,9 +1351,9 @@ pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
   }
   {
     ProfileScope prof("bwd_dq", s);
-    // 32-column waves with direct copies for bf16 at D = 96 in blocks of 64-token multiples;
-    // position mode "none" keeps the register-staged kernel (see the note on earlier
-    // direct-copy attempts in the design notes)
+    // 32-column waves with direct copies for bf16 at D = 96 in blocks of 64-token multiples.
+    // Position mode "none" keeps the register-staged kernel: earlier direct-copy versions of
+    // this kernel raised memory faults in that mode only, with the cause not found.
     if constexpr (sizeof(T) == 2 && DP == 96 && ONE_BLOCK) {
       if (d.D == 96 && a.pos_mode != PACK3D_POS_NONE) hipLaunchKernelGGL(k_bwd_dq32<96>, tiles, dim3(kThreads), 0, s, a);
       else hipLaunchKernelGGL((k_bwd_dq<T, DP, ONE_BLOCK>), tiles, dim3(kThreads), 0, s, a);

@@ -11,13 +11,14 @@
 // origin: every logit depends on coordinate differences only, so this changes no
 // logit and keeps the fp32 angles small.
 //
-// One workgroup per (block, head group, volume).  The block's tokens are gathered
+// k_rope_pool: one workgroup per (block, head group, volume).  The block's tokens are gathered
 // from packed order (perm); Q and K are rotated in fp32 and written with V in
 // canonical order [B, H, NC, Dp] (rows zero-padded to Dp, empty slots zero rows);
 // the block means of the rotated K and of V over the tokens present ([B, H, nblkp,
 // Dp], zero rows for empty and padding blocks) are summed in a fixed order from
-// LDS, so results are bitwise reproducible and independent of the packing.  HBM
-// bound: reads q, k, v once, writes the rotated Q, K and V once.
+// LDS, so results are bitwise reproducible and independent of the packing.
+// k_rope_pool_rows does the same with every head in one workgroup where rows need no
+// padding (below).  HBM bound: reads q, k, v once, writes the rotated Q, K and V once.
 #include <cmath>
 
 #include "layout.h"
@@ -231,6 +232,150 @@ __global__ __launch_bounds__(256) void k_rope_pool(RopeArgs a) {
   }
 }
 
+// The same pass with all heads in one workgroup, for rows without padding (Dp = D) whose
+// rotation pairs fall in whole 16-byte pieces.  One workgroup per (block, volume); a row
+// group of P threads covers one token's q, k and v rows whole (H * D contiguous elements
+// each in the packed input), each thread one rotation pair of VEC-element pieces of one
+// head, so every token's rows are read as full aligned runs.  A thread keeps the column
+// sums of its K~ and V pieces over the tokens of its row group; the R row groups' sums are
+// then added in a fixed order through LDS, so the block means stay bitwise reproducible
+// and independent of the packing.
+template <typename T, int GROUPS, bool ROTATE>
+__global__ __launch_bounds__(256) void k_rope_pool_rows(RopeArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  extern __shared__ char smem[];
+  const int blk = blockIdx.x, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int NC = a.NC, H = a.H, D = a.D, bvol = a.bvol;
+  const int gw = D / GROUPS, half = gw / 2, pchunks = half / VEC;
+  const int per_head = D / (2 * VEC);  // rotation-pair items per head
+  const int P = H * per_head;          // threads per row group (host: P <= 256)
+  const int R = 256 / P;               // row groups
+  const int r = tid / P, pi = tid - r * P;
+  const bool pool = a.pool != 0;
+  // LDS: src[bvol], rel[bvol][3] (int), then the partial sums [4 VEC][256] (float)
+  int* s_src = (int*)smem;
+  int* s_rel = s_src + bvol;
+  float* s_sum = (float*)(s_rel + 3 * bvol);
+
+  const int32_t* g = a.geom + b * G_FIELDS;
+  const int64_t tok0 = a.voff[b];
+  int base[3] = {0, 0, 0};
+  if (GROUPS == 3) {
+    const int nby = (g[G_EY] + a.by - 1) / a.by, nbx = (g[G_EX] + a.bx - 1) / a.bx;
+    base[0] = blk / (nby * nbx) * a.bz;
+    base[1] = (blk / nbx) % nby * a.by;
+    base[2] = blk % nbx * a.bx;
+  }
+  for (int t = tid; t < bvol; t += 256) {
+    const int src = a.perm[(int64_t)b * NC + blk * bvol + t];  // -1: empty slot
+    s_src[t] = src;
+    int rel[3] = {0, 0, 0};
+    if (src >= 0 && ROTATE) {
+      if (GROUPS == 3) {
+        rel[0] = base[0] + t / (a.by * a.bx);
+        rel[1] = base[1] + (t / a.bx) % a.by;
+        rel[2] = base[2] + t % a.bx;
+      } else {
+        rel[0] = src;
+      }
+    }
+    for (int gi = 0; gi < GROUPS; ++gi) {
+      const int rr = rel[gi];
+      s_rel[t * 3 + gi] = rr < 0 ? 0 : (rr >= a.trows ? a.trows - 1 : rr);
+    }
+  }
+  __syncthreads();
+
+  const int h = pi / per_head, j = pi - h * per_head;
+  const int ax = j / pchunks, p = j - ax * pchunks;
+  const int col1 = ax * gw + p * VEC, col2 = col1 + half;
+  float ks1[VEC], ks2[VEC], vs1[VEC], vs2[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) ks1[e] = ks2[e] = vs1[e] = vs2[e] = 0.f;
+  if (r < R) {
+    const T* q = (const T*)a.q;
+    const T* k = (const T*)a.k;
+    const T* v = (const T*)a.v;
+    const int64_t orow0 = ((int64_t)b * H + h) * NC + (int64_t)blk * bvol;
+    for (int t = r; t < bvol; t += R) {
+      const int src = s_src[t];
+      Vec<T, VEC> q1, q2, k1, k2, v1, v2;
+      if (src >= 0) {
+        const int64_t in_row = (tok0 + src) * a.in_stride + (int64_t)h * D;
+        q1 = *(const Vec<T, VEC>*)(q + in_row + col1);
+        q2 = *(const Vec<T, VEC>*)(q + in_row + col2);
+        k1 = *(const Vec<T, VEC>*)(k + in_row + col1);
+        k2 = *(const Vec<T, VEC>*)(k + in_row + col2);
+        v1 = *(const Vec<T, VEC>*)(v + in_row + col1);
+        v2 = *(const Vec<T, VEC>*)(v + in_row + col2);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) q1.v[e] = q2.v[e] = k1.v[e] = k2.v[e] = v1.v[e] = v2.v[e] = from_f<T>(0.f);
+      }
+      const float2* cs = a.tab + (int64_t)s_rel[t * 3 + ax] * half + p * VEC;
+      Vec<T, VEC> oq1, oq2, ok1, ok2;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float2 rot = ROTATE ? cs[e] : make_float2(1.f, 0.f);
+        const float x1 = to_f(q1.v[e]), x2 = to_f(q2.v[e]);
+        oq1.v[e] = ROTATE ? from_f<T>(x1 * rot.x - x2 * rot.y) : q1.v[e];
+        oq2.v[e] = ROTATE ? from_f<T>(x1 * rot.y + x2 * rot.x) : q2.v[e];
+        const float y1 = to_f(k1.v[e]), y2 = to_f(k2.v[e]);
+        ok1.v[e] = ROTATE ? from_f<T>(y1 * rot.x - y2 * rot.y) : k1.v[e];
+        ok2.v[e] = ROTATE ? from_f<T>(y1 * rot.y + y2 * rot.x) : k2.v[e];
+        // the block means average the rotated K as stored, and V
+        ks1[e] += to_f(ok1.v[e]);
+        ks2[e] += to_f(ok2.v[e]);
+        vs1[e] += to_f(v1.v[e]);
+        vs2[e] += to_f(v2.v[e]);
+      }
+      const int64_t out_row = (orow0 + t) * D;
+      *(Vec<T, VEC>*)((T*)a.qrot + out_row + col1) = oq1;
+      *(Vec<T, VEC>*)((T*)a.qrot + out_row + col2) = oq2;
+      *(Vec<T, VEC>*)((T*)a.krot + out_row + col1) = ok1;
+      *(Vec<T, VEC>*)((T*)a.krot + out_row + col2) = ok2;
+      *(Vec<T, VEC>*)((T*)a.vr + out_row + col1) = v1;
+      *(Vec<T, VEC>*)((T*)a.vr + out_row + col2) = v2;
+    }
+  }
+  if (!pool) return;
+  // partial sums [e][tid] (e: K~ piece 1, K~ piece 2, V piece 1, V piece 2, VEC each)
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    s_sum[(0 * VEC + e) * 256 + tid] = ks1[e];
+    s_sum[(1 * VEC + e) * 256 + tid] = ks2[e];
+    s_sum[(2 * VEC + e) * 256 + tid] = vs1[e];
+    s_sum[(3 * VEC + e) * 256 + tid] = vs2[e];
+  }
+  __syncthreads();
+  // mean over the tokens present (|b| on a full grid); an empty block's sums are 0
+  const int cnt = a.holes ? a.count[(int64_t)b * a.nblk + blk] : bvol;
+  const float inv = cnt > 0 ? 1.0f / (float)cnt : 0.f;
+  for (int it = tid; it < 4 * VEC * P; it += 256) {
+    const int e4 = it / P, qi = it - e4 * P;  // piece element, pair item
+    float sum = 0.f;
+    for (int rr = 0; rr < R; ++rr) sum += s_sum[e4 * 256 + rr * P + qi];  // row groups in order
+    const int hh = qi / per_head, jj = qi - hh * per_head;
+    const int aa = jj / pchunks, pp = jj - aa * pchunks;
+    const int which = e4 / VEC, el = e4 - which * VEC;
+    const int c = aa * gw + pp * VEC + (which & 1 ? half : 0) + el;
+    T* bar = which < 2 ? (T*)a.kbar : (T*)a.vbar;
+    const int64_t brow = ((int64_t)b * H + hh) * a.nblkp;
+    bar[(brow + blk) * D + c] = from_f<T>(sum * inv);
+    // zero the padding summaries nblk .. nblkp (there may be more of them than blocks)
+    for (int pad_blk = a.nblk + blk; pad_blk < a.nblkp; pad_blk += a.nblk) bar[(brow + pad_blk) * D + c] = from_f<T>(0.f);
+  }
+}
+
+// Threads of one row group of k_rope_pool_rows (0: the layout does not suit it).
+inline int rows_kernel_threads(const Dims& d) {
+  const int vec = 16 / (int)d.esize;
+  if (d.Dp != d.D || d.half % vec != 0) return 0;
+  const int p = d.H * d.D / (2 * vec);
+  return p <= 256 ? p : 0;
+}
+
 template <typename T, int GROUPS, bool ROTATE>
 void launch_mode(const Dims& d, const RopeArgs& a, dim3 grid, size_t lds, hipStream_t s) {
   int vec = 1;
@@ -248,6 +393,15 @@ void launch_mode(const Dims& d, const RopeArgs& a, dim3 grid, size_t lds, hipStr
 
 template <typename T>
 pack3d_status launch_typed(const Dims& d, const RopeArgs& a, const char* name, hipStream_t s) {
+  if (rows_kernel_threads(d) > 0) {
+    const size_t lds = sizeof(int) * 4 * d.bvol + (a.pool ? sizeof(float) * 4 * (16 / sizeof(T)) * 256 : 0);
+    const dim3 grid(d.nblk, 1, d.B);
+    ProfileScope prof(name, s);
+    if (d.pos_mode == PACK3D_POS_AXIAL) hipLaunchKernelGGL((k_rope_pool_rows<T, 3, true>), grid, dim3(256), lds, s, a);
+    else if (d.pos_mode == PACK3D_POS_PACKED_1D) hipLaunchKernelGGL((k_rope_pool_rows<T, 1, true>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((k_rope_pool_rows<T, 1, false>), grid, dim3(256), lds, s, a);
+    return check_launch("rope/pool");
+  }
   const int ntok = d.bvol < kChunk ? d.bvol : kChunk;
   // the staging tiles exist only to form the block means
   const size_t lds = sizeof(int) * 4 * d.bvol + (a.pool ? 2 * sizeof(T) * ntok * (d.Dp + 1) : 0);
