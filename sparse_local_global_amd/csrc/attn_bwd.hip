@@ -1275,7 +1275,7 @@ void k_bwd_dq32(BwdArgs a) {
     // S^T and dP^T for keys 32kh .. 32kh+31; dS = P (dP - delta), with -delta added here (a
     // register block of it as the accumulators' start would stay live across the loop)
     f32x16 s, dp;
-    score32_pair(S.k, qf, s, S.v, gf, dp, col, half, kh);
+    score32_pair_ahead<DP, 3>(S.k, qf, s, S.v, gf, dp, col, half, kh);
     if (mine != ~0u) mask_rows32(s, mine, half);
     bf16x8 pb[2];
 #pragma unroll

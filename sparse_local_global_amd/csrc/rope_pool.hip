@@ -298,45 +298,59 @@ __global__ __launch_bounds__(256) void k_rope_pool_rows(RopeArgs a) {
     const T* k = (const T*)a.k;
     const T* v = (const T*)a.v;
     const int64_t orow0 = ((int64_t)b * H + h) * NC + (int64_t)blk * bvol;
-    for (int t = r; t < bvol; t += R) {
+    // two tokens per trip, both tokens' loads issued before either is stored
+    auto load = [&](int t, Vec<T, VEC> (&x)[6]) {
       const int src = s_src[t];
-      Vec<T, VEC> q1, q2, k1, k2, v1, v2;
       if (src >= 0) {
         const int64_t in_row = (tok0 + src) * a.in_stride + (int64_t)h * D;
-        q1 = *(const Vec<T, VEC>*)(q + in_row + col1);
-        q2 = *(const Vec<T, VEC>*)(q + in_row + col2);
-        k1 = *(const Vec<T, VEC>*)(k + in_row + col1);
-        k2 = *(const Vec<T, VEC>*)(k + in_row + col2);
-        v1 = *(const Vec<T, VEC>*)(v + in_row + col1);
-        v2 = *(const Vec<T, VEC>*)(v + in_row + col2);
+        x[0] = *(const Vec<T, VEC>*)(q + in_row + col1);
+        x[1] = *(const Vec<T, VEC>*)(q + in_row + col2);
+        x[2] = *(const Vec<T, VEC>*)(k + in_row + col1);
+        x[3] = *(const Vec<T, VEC>*)(k + in_row + col2);
+        x[4] = *(const Vec<T, VEC>*)(v + in_row + col1);
+        x[5] = *(const Vec<T, VEC>*)(v + in_row + col2);
       } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) q1.v[e] = q2.v[e] = k1.v[e] = k2.v[e] = v1.v[e] = v2.v[e] = from_f<T>(0.f);
+        for (int i = 0; i < 6; ++i)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[i].v[e] = from_f<T>(0.f);
       }
+    };
+    auto store = [&](int t, const Vec<T, VEC> (&x)[6]) {
       const float2* cs = a.tab + (int64_t)s_rel[t * 3 + ax] * half + p * VEC;
       Vec<T, VEC> oq1, oq2, ok1, ok2;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
+        // each rotated value as one product rounded, then a fused multiply-add, so the bits
+        // do not depend on how the compiler contracts the expression
         const float2 rot = ROTATE ? cs[e] : make_float2(1.f, 0.f);
-        const float x1 = to_f(q1.v[e]), x2 = to_f(q2.v[e]);
-        oq1.v[e] = ROTATE ? from_f<T>(x1 * rot.x - x2 * rot.y) : q1.v[e];
-        oq2.v[e] = ROTATE ? from_f<T>(x1 * rot.y + x2 * rot.x) : q2.v[e];
-        const float y1 = to_f(k1.v[e]), y2 = to_f(k2.v[e]);
-        ok1.v[e] = ROTATE ? from_f<T>(y1 * rot.x - y2 * rot.y) : k1.v[e];
-        ok2.v[e] = ROTATE ? from_f<T>(y1 * rot.y + y2 * rot.x) : k2.v[e];
+        const float x1 = to_f(x[0].v[e]), x2 = to_f(x[1].v[e]);
+        oq1.v[e] = ROTATE ? from_f<T>(fmaf(x1, rot.x, -(x2 * rot.y))) : x[0].v[e];
+        oq2.v[e] = ROTATE ? from_f<T>(fmaf(x1, rot.y, x2 * rot.x)) : x[1].v[e];
+        const float y1 = to_f(x[2].v[e]), y2 = to_f(x[3].v[e]);
+        ok1.v[e] = ROTATE ? from_f<T>(fmaf(y1, rot.x, -(y2 * rot.y))) : x[2].v[e];
+        ok2.v[e] = ROTATE ? from_f<T>(fmaf(y1, rot.y, y2 * rot.x)) : x[3].v[e];
         // the block means average the rotated K as stored, and V
         ks1[e] += to_f(ok1.v[e]);
         ks2[e] += to_f(ok2.v[e]);
-        vs1[e] += to_f(v1.v[e]);
-        vs2[e] += to_f(v2.v[e]);
+        vs1[e] += to_f(x[4].v[e]);
+        vs2[e] += to_f(x[5].v[e]);
       }
       const int64_t out_row = (orow0 + t) * D;
       *(Vec<T, VEC>*)((T*)a.qrot + out_row + col1) = oq1;
       *(Vec<T, VEC>*)((T*)a.qrot + out_row + col2) = oq2;
       *(Vec<T, VEC>*)((T*)a.krot + out_row + col1) = ok1;
       *(Vec<T, VEC>*)((T*)a.krot + out_row + col2) = ok2;
-      *(Vec<T, VEC>*)((T*)a.vr + out_row + col1) = v1;
-      *(Vec<T, VEC>*)((T*)a.vr + out_row + col2) = v2;
+      *(Vec<T, VEC>*)((T*)a.vr + out_row + col1) = x[4];
+      *(Vec<T, VEC>*)((T*)a.vr + out_row + col2) = x[5];
+    };
+    for (int t = r; t < bvol; t += 2 * R) {
+      Vec<T, VEC> xa[6], xb[6];
+      const bool two = t + R < bvol;
+      load(t, xa);
+      if (two) load(t + R, xb);
+      store(t, xa);
+      if (two) store(t + R, xb);
     }
   }
   if (!pool) return;

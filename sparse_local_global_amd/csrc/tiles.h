@@ -305,6 +305,40 @@ __device__ inline void score32_pair(const RowTile<bf16, DP>& t1, const ColFrag32
   }
 }
 
+// score32_pair with its LDS reads scheduled NPRE ahead of the products that use them: the
+// first NPRE reads are issued together, then each product is followed by the next read.
+template <int DP, int NPRE>
+__device__ inline void score32_pair_ahead(const RowTile<bf16, DP>& t1, const ColFrag32<DP>& f1, f32x16& s1,
+                                          const RowTile<bf16, DP>& t2, const ColFrag32<DP>& f2, f32x16& s2, int col,
+                                          int half, int mt) {
+  using G = TileGeom<bf16, DP>;
+  constexpr int NK = DP / 16, NR = 2 * NK;
+  static_assert(NPRE > 0 && NPRE <= NR, "reads ahead");
+  const int be = G::base(col & 15, half) + G::off(col & 16, 0);
+  const int bo = G::base(col & 15, 2 + half) + G::off(col & 16, 0);
+  bf16x8 a1[NK], a2[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int o = (k & 1 ? bo : be) + G::off(32 * mt, 4 * (k >> 1));
+    a1[k] = *(const bf16x8*)(t1.x + o);
+    a2[k] = *(const bf16x8*)(t2.x + o);
+  }
+  s1 = f32x16{};
+  s2 = f32x16{};
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[k], f1.b[k], s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[k], f2.b[k], s2, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < NR - NPRE; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
+}
+
 // Rows 32mt .. 32mt+31 of one score tile: slot i = row 32mt + 8(i/4) + 4h + i%4 against
 // column (lane & 31).
 template <int DP>
