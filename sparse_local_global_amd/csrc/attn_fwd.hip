@@ -572,7 +572,8 @@ void k_attn_fwd32d(FwdArgs a) {
   auto compute = [&](auto sg, uint32_t mine, const RowsFrag32<DP>& vfr) {
     const FwdStage32<DP>& S = stage(sg);
     f32x16 sc;
-    score32_rows(S.k, f, sc, col, half, kh);
+    // the K reads run three ahead of their products (more would spill at three waves per SIMD)
+    score32_rows_ahead<DP, 3>(S.k, f, sc, col, half, kh);
     if (mine != ~0u) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {

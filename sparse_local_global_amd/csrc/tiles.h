@@ -313,7 +313,8 @@ __device__ inline void score32_pair_ahead(const RowTile<bf16, DP>& t1, const Col
                                           int half, int mt) {
   using G = TileGeom<bf16, DP>;
   constexpr int NK = DP / 16, NR = 2 * NK;
-  static_assert(NPRE > 0 && NPRE <= NR, "reads ahead");
+  constexpr int NA = NPRE < NR ? NPRE : NR;  // reads ahead
+  static_assert(NA > 0, "reads ahead");
   const int be = G::base(col & 15, half) + G::off(col & 16, 0);
   const int bo = G::base(col & 15, 2 + half) + G::off(col & 16, 0);
   bf16x8 a1[NK], a2[NK];
@@ -330,13 +331,37 @@ __device__ inline void score32_pair_ahead(const RowTile<bf16, DP>& t1, const Col
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[k], f1.b[k], s1, 0, 0, 0);
     s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[k], f2.b[k], s2, 0, 0, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);  // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);  // LDS reads
 #pragma unroll
-  for (int i = 0; i < NR - NPRE; ++i) {
+  for (int i = 0; i < NR - NA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NA, 0);
+}
+
+// score32_rows with its LDS reads scheduled NPRE ahead of the products that use them.
+template <int DP, int NPRE>
+__device__ inline void score32_rows_ahead(const RowTile<bf16, DP>& t, const ColFrag32<DP>& f, f32x16& s, int col,
+                                          int half, int mt) {
+  using G = TileGeom<bf16, DP>;
+  constexpr int NK = DP / 16;
+  constexpr int NA = NPRE < NK ? NPRE : NK;
+  const int be = G::base(col & 15, half) + G::off(col & 16, 0);
+  const int bo = G::base(col & 15, 2 + half) + G::off(col & 16, 0);
+  bf16x8 a[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) a[k] = *(const bf16x8*)(t.x + (k & 1 ? bo : be) + G::off(32 * mt, 4 * (k >> 1)));
+  s = f32x16{};
+#pragma unroll
+  for (int k = 0; k < NK; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], f.b[k], s, 0, 0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);
+#pragma unroll
+  for (int i = 0; i < NK - NA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NA, 0);
 }
 
 // Rows 32mt .. 32mt+31 of one score tile: slot i = row 32mt + 8(i/4) + 4h + i%4 against
