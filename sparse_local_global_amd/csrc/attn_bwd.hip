@@ -126,6 +126,66 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdArgs a) {
   }
 }
 
+// The same for bf16 rows without padding with every head in one workgroup: the workgroup
+// takes TPW consecutive canonical slots, and its items run over (slot, head, 8-element piece)
+// with the piece fastest, so consecutive threads read consecutive 16 bytes of a token's dO
+// and O rows (H * D contiguous elements each).  Each thread loads all three of its items
+// before it stores any.  The sums run in the same order as in k_bwd_pre (each piece, then
+// the pieces of a row in order), so the results are bitwise the same.
+constexpr int kPreItems = 3;  // items per thread
+
+__global__ __launch_bounds__(256) void k_bwd_pre_rows(BwdArgs a, int tpw) {
+  constexpr int VEC = 8;
+  extern __shared__ char smem[];
+  float* part = (float*)smem;  // [tpw][H][nch] piece dot products
+  const int H = a.H, D = a.D, N = a.NC, nch = D / VEC;
+  const int per_slot = H * nch;
+  const int tid = threadIdx.x, b = blockIdx.y;
+  const int kappa0 = blockIdx.x * tpw;
+  const int64_t tok0 = a.voff[b];
+  Vec<bf16, VEC> g[kPreItems], o[kPreItems];
+#pragma unroll
+  for (int u = 0; u < kPreItems; ++u) {
+    const int it = tid + 256 * u, q = it / per_slot, rem = it - q * per_slot;
+    const int h = rem / nch, c = rem - h * nch;
+    const int kappa = kappa0 + q;
+    const int src = q < tpw && kappa < N ? a.perm[(int64_t)b * N + kappa] : -1;
+    if (src >= 0) {
+      const int64_t in = ((tok0 + src) * H + h) * D + c * VEC;
+      g[u] = *(const Vec<bf16, VEC>*)((const bf16*)a.dout + in);
+      o[u] = *(const Vec<bf16, VEC>*)((const bf16*)a.out + in);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) g[u].v[e] = o[u].v[e] = (bf16)0.f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPreItems; ++u) {
+    const int it = tid + 256 * u, q = it / per_slot, rem = it - q * per_slot;
+    const int h = rem / nch, c = rem - h * nch;
+    const int kappa = kappa0 + q;
+    if (q >= tpw || kappa >= N) continue;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc += (float)g[u].v[e] * (float)o[u].v[e];
+    part[it] = acc;
+    *(Vec<bf16, VEC>*)((bf16*)a.doc + (((int64_t)b * H + h) * N + kappa) * D + c * VEC) = g[u];
+  }
+  __syncthreads();
+  if (tid < tpw * H) {
+    const int q = tid / H, h = tid - q * H, kappa = kappa0 + q;
+    if (kappa < N) {
+      const int64_t bh = (int64_t)b * H + h;
+      const int src = a.perm[(int64_t)b * N + kappa];
+      float s = 0.f;
+      for (int c = 0; c < nch; ++c) s += part[(q * H + h) * nch + c];
+      a.ndelta[bh * N + kappa] = -s;
+      // log2 units; +inf for an empty slot makes every probability of that row 0
+      a.lsec[bh * N + kappa] = src >= 0 ? a.lse[bh * a.Nmax + src] * kLog2e : INFINITY;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // Epilogue shared by bwd_local and bwd_dq: rows of fp32 gradients staged in LDS
 // (canonical rows row0 .. row0+nrows), optionally rotated back by R^T, written in
@@ -1371,7 +1431,14 @@ pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {
 
 template <typename T>
 pack3d_status launch_typed(const Dims& d, const BwdArgs& a, hipStream_t s) {
-  {
+  // all heads per workgroup where bf16 rows need no padding and a slot's pieces fit the items
+  const int per_slot = d.H * (d.D / 8);
+  const int tpw = sizeof(T) == 2 && d.Dp == d.D && d.half % 8 == 0 ? 256 * kPreItems / per_slot : 0;
+  if (tpw > 0) {
+    const dim3 grid((unsigned)((d.NC + tpw - 1) / tpw), d.B);
+    ProfileScope prof("bwd_pre", s);
+    hipLaunchKernelGGL(k_bwd_pre_rows, grid, dim3(256), sizeof(float) * 256 * kPreItems, s, a, tpw);
+  } else {
     const int ntok = d.bvol < kTile ? d.bvol : kTile;
     int vec = 1;
     const int cap = 16 / (int)sizeof(T);
