@@ -840,10 +840,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       ++iss_q;
     }
     const int w = wave_id(), r = 16 * w + (lane & 15);
-    // (issue_at in this generic lambda costs another kernel's host-side stub, see
-    // bwd_local32; the row form serves both layouts)
-    dma.issue(qrot, S.q, nrow, [&](int rr) { return (row0 + rr) * DP; });
-    dma.issue(doc, S.g, nrow, [&](int rr) { return (row0 + rr) * DP; });
+    if (nrow == kTile) {
+      dma.issue_at(qrot, S.q, (uint32_t)row0 * DP);
+      dma.issue_at(doc, S.g, (uint32_t)row0 * DP);
+    } else {
+      dma.issue(qrot, S.q, nrow, [&](int rr) { return (row0 + rr) * DP; });
+      dma.issue(doc, S.g, nrow, [&](int rr) { return (row0 + rr) * DP; });
+    }
     const uint32_t off = r < nrow ? (uint32_t)(row0 + r) * 4u : 0x80000000u;
     issue_rows16(lsec, &S.lse2[16 * w], off);
     issue_rows16(dlt, &S.ndelta[16 * w], off);
@@ -1311,10 +1314,8 @@ void k_bwd_dq32(BwdArgs a) {
     }
     const size_t bytes = loc ? bytes_loc : bytes_sum;
     const Src ks(loc ? kq : kbq, bytes), vs(loc ? vq : vbq, bytes);
-    // (issue_at here would cost another kernel's host-side stub, see bwd_local32; the row
-    // form with every row valid copies the same bytes)
-    dma.issue(ks, S.k, kTile, [&](int r) { return (int)(row0 + r) * DP; });
-    dma.issue(vs, S.v, kTile, [&](int r) { return (int)(row0 + r) * DP; });
+    dma.issue_at(ks, S.k, row0 * DP);
+    dma.issue_at(vs, S.v, row0 * DP);
   };
   // this wave's live key rows of tile t (bit r: row 32kh + r)
   auto live_rows = [&](int t) -> uint32_t {
@@ -1382,6 +1383,20 @@ void k_bwd_dq32(BwdArgs a) {
     }
   dq32_epilogue96(a, dq, b, h, qrow0 + qloc, true, half);
 }
+
+// Explicit instantiations of the 32-column kernels: when several kernels of this file call
+// the copy helpers from generic lambdas, the host compilation can leave out the launch stub
+// of some of them with no diagnostic (the library then fails to load); instantiating every
+// one here makes the host side emit all of them.
+template __global__ void k_bwd_local32<32, true>(BwdArgs);
+template __global__ void k_bwd_local32<96, true>(BwdArgs);
+template __global__ void k_bwd_local32<32, false>(BwdArgs);
+template __global__ void k_bwd_local32<96, false>(BwdArgs);
+template __global__ void k_bwd_summary32<32, true>(BwdArgs);
+template __global__ void k_bwd_summary32<96, true>(BwdArgs);
+template __global__ void k_bwd_summary32<32, false>(BwdArgs);
+template __global__ void k_bwd_summary32<96, false>(BwdArgs);
+template __global__ void k_bwd_dq32<96>(BwdArgs);
 
 template <typename T, int DP, bool ONE_BLOCK>
 pack3d_status launch_dp(const Dims& d, const BwdArgs& a, hipStream_t s) {

@@ -485,8 +485,9 @@ void k_attn_fwd32d(FwdArgs a) {
     if constexpr (decltype(sg)::value == 0) return s0;
     else return s1;
   };
-  // (the host-side instantiation of this generic lambda fails silently when one branch
-  // calls issue_at and another issue, so each instantiation uses only one of them)
+  // (each instantiation of this generic lambda calls only one of issue_at and issue: with
+  // both, the host compilation has left out launch stubs, see the explicit instantiations
+  // in attn_bwd.hip)
   const bf16* kq = (const bf16*)a.krot + bh * N * DP;
   const bf16* vq = (const bf16*)a.vr + bh * N * DP;
   const bf16* kbq = (const bf16*)a.kbar + bh * a.nblkp * DP;

@@ -552,26 +552,28 @@ struct TileDma {
   static_assert(kTile * CH % NT == 0, "tile slots must spread evenly over the threads");
   static constexpr int ROUNDS = kTile * CH / NT;  // vector-memory instructions per tile and wave
   int row[ROUNDS];   // tile row of this lane's slot in round i
-  int loff[ROUNDS];  // element offset of that slot's logical chunk in a dense [64][DP] tile
+  int loffb[ROUNDS]; // byte offset of that slot's logical chunk in a dense [64][DP] tile
   __device__ inline TileDma() {
 #pragma unroll
     for (int i = 0; i < ROUNDS; ++i) {
       const int p = i * NT + (int)threadIdx.x;  // = (i * NT / 64 + wave) * 64 + lane
       const int r = p / CH, c = (p - r * CH) ^ G::swz(r);
       row[i] = r;
-      loff[i] = r * DP + (c << 3);
+      loffb[i] = (r * DP + (c << 3)) * 2;
     }
   }
   __device__ static inline lds_void* dst(RowTile<bf16, DP>& t, int i, int w) {
     return (lds_void*)((lds_char*)t.x + (i * NT + 64 * w) * 16);
   }
   // Tile rows contiguous from element `base` of src (the same on every lane); all rows valid.
+  // The uniform part of the address goes in the scalar offset, so a copy costs no vector
+  // instruction besides itself.
   __device__ inline void issue_at(const Src& src, RowTile<bf16, DP>& t, uint32_t base) const {
     const int w = wave_id();
     const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base * 2u));
 #pragma unroll
     for (int i = 0; i < ROUNDS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, dst(t, i, w), 16, b + (uint32_t)loff[i] * 2u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, dst(t, i, w), 16, (uint32_t)loffb[i], b, 0, 0);
   }
   // Row r from element offset rowoff(r) of src (r < valid); rows past `valid` become zero.
   template <typename RowOff>
@@ -580,7 +582,7 @@ struct TileDma {
 #pragma unroll
     for (int i = 0; i < ROUNDS; ++i) {
       const int r = row[i];
-      const uint32_t off = r < valid ? (uint32_t)(rowoff(r) + loff[i] - r * DP) * 2u : 0x80000000u;
+      const uint32_t off = r < valid ? (uint32_t)(rowoff(r) + (loffb[i] >> 1) - r * DP) * 2u : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, dst(t, i, w), 16, off, 0, 0, 0);
     }
   }
