@@ -226,9 +226,10 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-sample-blocks", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true", help="skip the hipBLASLt GEMM reference")
-    ap.add_argument("--profile-pass", choices=["step", "forward", "windowed"], default=None,
-                    help="only run warmup + steps of one pass (the step, the forward, or the windowed-only "
-                         "forward) and print its time: for profiler runs, so each pass has its own rows")
+    ap.add_argument("--profile-pass", choices=["step", "forward", "windowed", "gemm"], default=None,
+                    help="only run warmup + steps of one pass (the step, the forward, the windowed-only "
+                         "forward, or the hipBLASLt reference GEMM) and print its time: for profiler runs, so "
+                         "each pass has its own rows")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for HBM counters)")
     args = ap.parse_args(argv)
@@ -240,6 +241,11 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+    if args.profile_pass == "gemm":
+        # the hipBLASLt reference GEMM alone, for the matrix-core counters of a plain GEMM
+        ms = gemm_ceiling(args.steps)["ms"]
+        print(json.dumps({"profile_pass": "gemm", "ms": ms, "steps": args.steps}))
+        return 0
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
